@@ -1,0 +1,296 @@
+/*
+ * oracle.c -- plain, slow FP64 CPU reference for E4M3 paged speculative-verify
+ * attention with split partials.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
+ * this file. It is used by tests/, by __graft_entry__.smoke() and by the
+ * cpu_baseline leg of bench.py. It shares no code, header, table or constant
+ * with the HIP library under paged_fp8_split_amd/.
+ *
+ * What it computes follows the pages' statement of the method:
+ *  - "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+ *    final-status section (revision 3 bullet): every KV partition keeps its
+ *    running max, its sum and its *unnormalized* PV product until one final
+ *    combine, which rescales the partials and normalizes once.
+ *  - "[Kernel] Finalize the audited TP2 DFlash2 31/29 ms endpoint", Purpose:
+ *    keys are consumed in 64-key partitions in a fixed (ascending) order;
+ *    Test Result: an exact E4M3 decoder checked over all byte values and an
+ *    FP64 reference.
+ *  - "[Bugfix] Use FP32 state and E4M3 defaults for DFlash2", Purpose: KV is
+ *    stored as FP8 E4M3, the query and the final activations are FP16.
+ *
+ * Readings where the pages are silent (each is listed in the design doc):
+ *  - E4M3 is the OCP "FN" variant: bias 7, no infinities, S.1111.111 = NaN,
+ *    largest finite 448.
+ *  - A request's live length L includes its q draft tokens; draft row i
+ *    (0-based) sees the first n_i = L - q + i + 1 tokens (clamped to [0, L]).
+ *    A row that sees no token outputs +0.0.
+ *  - Partitions are absolute token ranges [p*T, (p+1)*T) of the row.
+ *  - Scales multiply the decoded bytes exactly (no re-rounding).
+ *
+ * Everything here is FP64 with plain loops in the order the method states:
+ * decode, score, per-partition (max, sum, unnormalized PV), then combine.
+ * Built with -O2 and without -ffast-math (the build script fixes the flags).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_NOMEM (-2)
+
+/* OCP E4M3FN byte -> exact value. s = sign bit, e = 4-bit biased exponent,
+ * m = 3-bit mantissa. e == 0 is subnormal: m/8 * 2^(1-7). e == 15 with m == 7
+ * is NaN; every other code is normal: (1 + m/8) * 2^(e-7). */
+double oracle_e4m3_value(uint32_t byte) {
+    const int s = (int)((byte >> 7) & 1u);
+    const int e = (int)((byte >> 3) & 15u);
+    const int m = (int)(byte & 7u);
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, 1 - 7);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* IEEE binary16 bit pattern -> exact value. */
+double oracle_fp16_value(uint32_t bits) {
+    const int s = (int)((bits >> 15) & 1u);
+    const int e = (int)((bits >> 10) & 31u);
+    const int m = (int)(bits & 1023u);
+    double mag;
+    if (e == 31) {
+        if (m) return NAN;
+        return s ? -INFINITY : INFINITY;
+    }
+    if (e == 0)
+        mag = ldexp((double)m, -24);
+    else
+        mag = ldexp(1024.0 + (double)m, e - 25);
+    return s ? -mag : mag;
+}
+
+/* Fill out[0..255] with the decoded value of every byte. */
+void oracle_e4m3_table(double* out) {
+    for (uint32_t b = 0; b < 256; ++b) out[b] = oracle_e4m3_value(b);
+}
+
+/* Number of keys draft row i of a request with live length L may attend to. */
+int64_t oracle_visible_keys(int64_t live_len, int32_t q, int32_t row) {
+    int64_t n = live_len - (int64_t)q + (int64_t)row + 1;
+    if (n < 0) n = 0;
+    if (n > live_len) n = live_len;
+    return n;
+}
+
+/*
+ * The verify attention.
+ *
+ * Shapes (all host memory):
+ *   q_fp16      [batch, q, num_q_heads, head_dim]  IEEE half bit patterns
+ *   k_pool/v_pool  byte pools addressed as
+ *                  page*page_stride + slot*token_stride + kv_head*head_stride + d
+ *   k_scale/v_scale [num_kv_heads] FP32
+ *   block_table [batch, max_pages_per_row] physical page of each logical page
+ *   live_len    [batch]
+ *   head_map    [num_q_heads] query head -> KV head
+ *   unit_mask   [batch * num_q_heads] or NULL: compute only units whose mask
+ *               byte is non-zero (others are left untouched)
+ *   out         [batch, q, num_q_heads, head_dim] FP64 (unrounded result)
+ *
+ * partition_tokens <= 0 means a single partition per row (the unsplit
+ * softmax). Returns ORACLE_OK or a negative error code.
+ */
+int oracle_verify(int32_t batch, int32_t q, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t page_size, int32_t max_pages_per_row,
+                  int32_t num_pool_pages, int32_t partition_tokens, int64_t page_stride,
+                  int64_t token_stride, int64_t head_stride, const uint16_t* q_fp16,
+                  const uint8_t* k_pool, const uint8_t* v_pool, const float* k_scale,
+                  const float* v_scale, const int32_t* block_table, const int32_t* live_len,
+                  const int32_t* head_map, const uint8_t* unit_mask, double sm_scale,
+                  double* out, int32_t num_threads) {
+    if (batch < 0 || q < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        page_size < 1 || max_pages_per_row < 0 || num_pool_pages < 0)
+        return ORACLE_ERR_ARG;
+    if (!q_fp16 || !k_pool || !v_pool || !k_scale || !v_scale || !block_table || !live_len ||
+        !head_map || !out)
+        return ORACLE_ERR_ARG;
+    for (int32_t h = 0; h < num_q_heads; ++h)
+        if (head_map[h] < 0 || head_map[h] >= num_kv_heads) return ORACLE_ERR_ARG;
+
+    double table[256];
+    oracle_e4m3_table(table);
+
+    const int64_t capacity = (int64_t)max_pages_per_row * page_size;
+    const int64_t units = (int64_t)batch * num_q_heads;
+    int status = ORACLE_OK;
+
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        double* khat = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        double* vhat = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        double* part_m = NULL;
+        double* part_l = NULL;
+        double* part_a = NULL;
+        double* sbuf = NULL;
+        int64_t part_cap = 0;
+        int64_t sbuf_cap = 0;
+        int local_err = (!qrow || !khat || !vhat || !acc);
+        int bad_page = 0;
+
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t unit = 0; unit < units * q; ++unit) {
+            if (local_err || bad_page) continue;
+            const int64_t bh = unit / q;
+            const int32_t row = (int32_t)(unit % q);
+            const int32_t b = (int32_t)(bh / num_q_heads);
+            const int32_t h = (int32_t)(bh % num_q_heads);
+            if (unit_mask && !unit_mask[bh]) continue;
+            const int32_t g = head_map[h];
+            double* dst = out + (((int64_t)b * q + row) * num_q_heads + h) * head_dim;
+
+            int64_t L = live_len[b];
+            if (L < 0) L = 0;
+            if (L > capacity) L = capacity;
+            const int64_t n = oracle_visible_keys(L, q, row);
+            if (n == 0) {
+                for (int32_t d = 0; d < head_dim; ++d) dst[d] = 0.0;
+                continue;
+            }
+
+            /* The draft query row, FP16 -> FP64 exactly. */
+            const uint16_t* qsrc = q_fp16 + (((int64_t)b * q + row) * num_q_heads + h) * head_dim;
+            for (int32_t d = 0; d < head_dim; ++d) qrow[d] = oracle_fp16_value(qsrc[d]);
+
+            const int64_t T = partition_tokens > 0 ? partition_tokens : n;
+            const int64_t nparts = (n + T - 1) / T;
+            if (nparts > part_cap) {
+                free(part_m);
+                free(part_l);
+                free(part_a);
+                part_m = (double*)malloc(sizeof(double) * (size_t)nparts);
+                part_l = (double*)malloc(sizeof(double) * (size_t)nparts);
+                part_a = (double*)malloc(sizeof(double) * (size_t)nparts * (size_t)head_dim);
+                part_cap = nparts;
+                if (!part_m || !part_l || !part_a) {
+                    local_err = 1;
+                    part_cap = 0;
+                    continue;
+                }
+            }
+
+            if (T > sbuf_cap) {
+                free(sbuf);
+                sbuf = (double*)malloc(sizeof(double) * (size_t)T);
+                sbuf_cap = T;
+                if (!sbuf) {
+                    local_err = 1;
+                    sbuf_cap = 0;
+                    continue;
+                }
+            }
+
+            /* Per partition, ascending: max score, sum of exp, unnormalized PV. */
+            for (int64_t p = 0; p < nparts; ++p) {
+                const int64_t j0 = p * T;
+                const int64_t j1 = (j0 + T < n) ? j0 + T : n;
+                double* a = part_a + p * head_dim;
+                /* scores of the partition's keys and their max */
+                double m = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    const int32_t page = block_table[(int64_t)b * max_pages_per_row + j / page_size];
+                    if (page < 0 || page >= num_pool_pages) {
+                        bad_page = 1;
+                        break;
+                    }
+                    const int64_t base = (int64_t)page * page_stride + (j % page_size) * token_stride +
+                                         (int64_t)g * head_stride;
+                    double s = 0.0;
+                    for (int32_t d = 0; d < head_dim; ++d) {
+                        khat[d] = table[k_pool[base + d]] * (double)k_scale[g];
+                        s += qrow[d] * khat[d];
+                    }
+                    s *= sm_scale;
+                    sbuf[j - j0] = s;
+                    if (s > m) m = s;
+                }
+                if (bad_page) break;
+                /* weights relative to that max: their sum and the unnormalized PV */
+                double l = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d) a[d] = 0.0;
+                for (int64_t j = j0; j < j1; ++j) {
+                    const int32_t page = block_table[(int64_t)b * max_pages_per_row + j / page_size];
+                    const int64_t base = (int64_t)page * page_stride + (j % page_size) * token_stride +
+                                         (int64_t)g * head_stride;
+                    const double w = exp(sbuf[j - j0] - m);
+                    l += w;
+                    for (int32_t d = 0; d < head_dim; ++d) {
+                        vhat[d] = table[v_pool[base + d]] * (double)v_scale[g];
+                        a[d] += w * vhat[d];
+                    }
+                }
+                part_m[p] = m;
+                part_l[p] = l;
+            }
+
+            if (bad_page) continue;
+
+            /* Final combine: rescale each partition to the global max, sum in
+             * partition order, normalize once. */
+            double M = -INFINITY;
+            for (int64_t p = 0; p < nparts; ++p)
+                if (part_m[p] > M) M = part_m[p];
+            double l = 0.0;
+            for (int32_t d = 0; d < head_dim; ++d) acc[d] = 0.0;
+            for (int64_t p = 0; p < nparts; ++p) {
+                const double f = exp(part_m[p] - M);
+                l += f * part_l[p];
+                const double* a = part_a + p * head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) acc[d] += f * a[d];
+            }
+            for (int32_t d = 0; d < head_dim; ++d) dst[d] = acc[d] / l;
+        }
+
+        if (local_err) {
+#pragma omp atomic write
+            status = ORACLE_ERR_NOMEM;
+        }
+        if (bad_page) {
+#pragma omp atomic write
+            status = ORACLE_ERR_ARG;
+        }
+        free(qrow);
+        free(khat);
+        free(vhat);
+        free(acc);
+        free(part_m);
+        free(part_l);
+        free(part_a);
+        free(sbuf);
+    }
+    return status;
+}
+
+/* Threads an OpenMP parallel region would use (for reporting). */
+int32_t oracle_max_threads(void) {
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

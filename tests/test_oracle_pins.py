@@ -1,0 +1,303 @@
+"""Pins for the FP64 oracle: checks against things other than the oracle itself.
+
+Each test ties the oracle to a library routine it does not use (torch's FP8 and
+FP16 decoders, torch's scaled-dot-product attention in float64), to a closed
+form, or to an invariance the mathematics fixes. Together they are chosen so
+that a plausible slip in the oracle (a wrong causal offset, a dropped scale, a
+swapped K/V or head index, a wrong partition fold) fails at least one of them;
+``test_pins_detect_planted_mistakes`` shows that directly.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from paged_fp8_split_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoders --
+
+def test_e4m3_decode_matches_torch_on_all_bytes():
+    ours = oracle.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.isnan(ours).sum() == 2  # 0x7F and 0xFF only (the FN variant)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    # signs: 0x80 is -0.0, every byte b|0x80 is the negation of b
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+    assert np.array_equal(ours[0x80:][fin[:128]], -ours[:128][fin[:128]])
+
+
+def test_e4m3_range_matches_absmax_over_448_recipe():
+    # the workloads quantize with scale = absmax / 448: 448 must be the largest
+    # finite code and 2^-9 the smallest positive one
+    t = oracle.e4m3_table()
+    fin = t[~np.isnan(t)]
+    assert fin.max() == 448.0 and t[0x7E] == 448.0
+    assert fin[fin > 0].min() == 2.0 ** -9 and t[0x01] == 2.0 ** -9
+    assert t[0x38] == 1.0 and t[0x39] == 1.125 and t[0x08] == 2.0 ** -6
+
+
+def test_fp16_decode_matches_numpy_on_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    lib = oracle._load()
+    ours = np.array([lib.oracle_fp16_value(int(b)) for b in bits])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+# ------------------------------------------------ dense reference (library) --
+
+def _dense_kv(w, pool, scale, b, g, L):
+    """Gather request b / KV head g as a dense float64 [L, D] tensor using
+    torch's FP8 decoder (independent of the oracle's table)."""
+    view = w.pool_view(pool)
+    t = np.arange(L)
+    raw = np.ascontiguousarray(view[w.block_table[b, t // w.page_size], t % w.page_size, g])
+    dec = torch.from_numpy(raw).view(torch.float8_e4m3fn).to(torch.float64)
+    return dec * float(scale[g])
+
+
+def sdpa_reference(w):
+    """torch scaled_dot_product_attention (float64, CPU) with an explicit
+    bottom-right causal mask; rows with no visible key are set to 0."""
+    out = np.zeros((w.batch, w.q, w.num_q_heads, w.head_dim))
+    for b in range(w.batch):
+        L = int(np.clip(w.live_len[b], 0, w.capacity))
+        if L == 0:
+            continue
+        i = torch.arange(w.q)[:, None]
+        j = torch.arange(L)[None, :]
+        mask = j <= (L - w.q + i)
+        for h in range(w.num_q_heads):
+            g = int(w.head_map[h])
+            K = _dense_kv(w, w.k_pool, w.k_scale, b, g, L)
+            V = _dense_kv(w, w.v_pool, w.v_scale, b, g, L)
+            Q = torch.from_numpy(w.q_fp16[b, :, h, :].astype(np.float64))
+            o = F.scaled_dot_product_attention(Q[None, None], K[None, None], V[None, None],
+                                               attn_mask=mask[None, None], scale=w.sm_scale)[0, 0]
+            o = o.numpy()
+            empty = ~mask.any(dim=1).numpy()
+            o[empty] = 0.0
+            out[b, :, h, :] = o
+    return out
+
+
+def _rel(a, b):
+    return np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300)
+
+
+SMALL = [
+    dict(batch=1, q=1, num_q_heads=1, num_kv_heads=1, head_dim=16, page_size=16, lengths=[37]),
+    dict(batch=2, q=3, num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16, lengths=[50, 2]),
+    dict(batch=3, q=8, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32, lengths=[300, 8, 0]),
+    dict(batch=2, q=16, num_q_heads=4, num_kv_heads=1, head_dim=16, page_size=16, lengths=[129, 5]),
+    dict(batch=1, q=4, num_q_heads=6, num_kv_heads=1, head_dim=32, page_size=48, lengths=[211],
+         token_pad=16, page_pad=48),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_oracle_matches_torch_sdpa(case):
+    w = W.build(seed=100 + case, **SMALL[case])
+    ours = oracle.verify(w)
+    ref = sdpa_reference(w)
+    assert np.all(np.isfinite(ours))
+    assert _rel(ours, ref) < 1e-13
+    assert np.abs(ours - ref).max() < 1e-12
+
+
+def test_oracle_matches_torch_sdpa_with_outliers_and_pow2_scales():
+    w = W.build(seed=7, batch=2, q=8, num_q_heads=8, num_kv_heads=4, head_dim=32, page_size=16,
+                lengths=[260, 97], outlier_frac=0.05, scale_mode="pow2", pow2_scale_exps=[-6, -3, 1, 4])
+    assert _rel(oracle.verify(w), sdpa_reference(w)) < 1e-13
+
+
+# ------------------------------------------------------------ closed forms --
+
+def test_single_visible_key_returns_that_value_row():
+    # L == q: draft row 0 sees exactly key 0, so its output is V-hat of key 0
+    w = W.build(seed=3, batch=1, q=4, num_q_heads=2, num_kv_heads=1, head_dim=32, page_size=16, lengths=[4])
+    out = oracle.verify(w)
+    v0 = _dense_kv(w, w.v_pool, w.v_scale, 0, 0, 1).numpy()[0]
+    for h in range(2):
+        assert np.array_equal(out[0, 0, h], v0)
+
+
+def test_uniform_scores_give_the_mean_of_visible_values():
+    w = W.build(seed=4, batch=1, q=8, num_q_heads=2, num_kv_heads=1, head_dim=16, page_size=16,
+                lengths=[100], zero_k_heads=[(0, 0)])
+    out = oracle.verify(w)
+    V = _dense_kv(w, w.v_pool, w.v_scale, 0, 0, 100).numpy()
+    for i in range(8):
+        n = 100 - 8 + i + 1
+        ref = V[:n].mean(axis=0)
+        assert np.abs(out[0, i, 0] - ref).max() <= 1e-15 * np.abs(ref).max() * 4
+
+
+def test_dominating_key_wins_exactly():
+    # one key scores > 800 above all others: exp underflows to 0 for the rest,
+    # so the output is exactly that key's V-hat
+    w = W.build(seed=5, batch=1, q=1, num_q_heads=1, num_kv_heads=1, head_dim=16, page_size=16, lengths=[40],
+                zero_k_heads=[(0, 0)])
+    w.q_fp16[...] = np.float16(240.0)
+    view = w.pool_view(w.k_pool)
+    j = 17
+    view[w.block_table[0, j // 16], j % 16, 0, :] = 0x7E  # 448
+    w.k_scale[:] = 1.0
+    out = oracle.verify(w)
+    vj = _dense_kv(w, w.v_pool, w.v_scale, 0, 0, 40).numpy()[j]
+    assert np.array_equal(out[0, 0, 0], vj)
+
+
+@pytest.mark.parametrize("count,expect_up", [(4, False), (12, True), (20, False), (28, True)])
+def test_exact_fp16_midpoints(count, expect_up):
+    # K = 0 -> uniform weights; V = 1.0 except `count` of n = 1024 keys at
+    # 1.125, so the mean is 1 + count * 2^-13, an exact FP16 tie when count/4
+    # is odd. The oracle must land on the tie exactly; RNE picks the even side.
+    n = 1024
+    w = W.build(seed=6, batch=1, q=1, num_q_heads=1, num_kv_heads=1, head_dim=8, page_size=64, lengths=[n],
+                midpoint={"b": 0, "g": 0, "counts": [count]}, scale_mode="pow2", pow2_scale_exps=[-6])
+    out = oracle.verify(w)[0, 0, 0]
+    exact = (1.0 + count * 2.0 ** -13) * 2.0 ** -6
+    assert np.all(out == exact)
+    r = np.float16(out[0])  # numpy's correctly rounded FP64 -> FP16
+    assert abs(float(r) - exact) == 2.0 ** -17  # the tie sits half an FP16 ulp (2^-16 at 2^-6) away
+    assert int(np.array(r).view(np.uint16)) & 1 == 0  # ties go to the even neighbour
+    assert (float(r) > exact) == expect_up
+
+
+# ------------------------------------------------------------ invariances --
+
+@pytest.mark.parametrize("T", [0, 1, 3, 16, 64, 1000])
+def test_partition_size_invariance(T):
+    w = W.build(seed=8, batch=2, q=8, num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16, lengths=[301, 64])
+    ref = oracle.verify(w, partition_tokens=0)
+    assert _rel(oracle.verify(w, partition_tokens=T), ref) < 1e-13
+
+
+def test_page_relocation_invariance_is_bitwise():
+    w = W.build(seed=9, batch=3, q=8, num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16,
+                lengths=[200, 33, 0])
+    a = oracle.verify(w)
+    b = oracle.verify(W.relocate(w, 1234))
+    assert np.array_equal(a, b)
+
+
+def test_tail_sentinel_invariance_is_bitwise():
+    w = W.build(seed=10, batch=2, q=8, num_q_heads=4, num_kv_heads=1, head_dim=32, page_size=16, lengths=[77, 9],
+                token_pad=16)
+    a = oracle.verify(W.set_tail_sentinel(w, W.SENTINEL_NAN))
+    b = oracle.verify(W.set_tail_sentinel(w, W.SENTINEL_MAX))
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b)
+
+
+def test_power_of_two_scalings_are_exact():
+    w = W.build(seed=11, batch=1, q=8, num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16, lengths=[150])
+    a = oracle.verify(w)
+    w2 = w.copy()
+    w2.v_scale = (w.v_scale * np.float32(8.0)).astype(np.float32)
+    assert np.array_equal(oracle.verify(w2), a * 8.0)
+    w3 = w.copy()  # k_scale * 2 with sm_scale / 2 leaves every score unchanged
+    w3.k_scale = (w.k_scale * np.float32(2.0)).astype(np.float32)
+    assert np.array_equal(oracle.verify(w3, sm_scale=w.sm_scale / 2), a)
+
+
+def test_causality_and_live_length():
+    w = W.build(seed=12, batch=1, q=8, num_q_heads=2, num_kv_heads=1, head_dim=16, page_size=16, lengths=[90])
+    a = oracle.verify(w)
+    # changing the last live key only affects the last draft row
+    w2 = w.copy()
+    view_k, view_v = w2.pool_view(w2.k_pool), w2.pool_view(w2.v_pool)
+    j = 89
+    view_k[w2.block_table[0, j // 16], j % 16, 0, :] ^= 0x01
+    view_v[w2.block_table[0, j // 16], j % 16, 0, :] ^= 0x01
+    b = oracle.verify(w2)
+    assert np.array_equal(a[0, :7], b[0, :7])
+    assert not np.array_equal(a[0, 7], b[0, 7])
+    # rows of a retired request (L = 0) and rows that see nothing (L < q) are +0
+    w3 = w.copy()
+    w3.live_len[:] = 5
+    c = oracle.verify(w3)
+    assert np.all(c[0, :3] == 0) and np.all(np.signbit(c[0, :3]) == False)  # noqa: E712
+    assert np.all(c[0, 3:] != 0)
+
+
+def test_head_map_and_batch_independence():
+    w = W.build(seed=13, batch=2, q=4, num_q_heads=4, num_kv_heads=2, head_dim=16, page_size=16, lengths=[70, 40])
+    a = oracle.verify(w)
+    # swap the two KV heads in both pools and in the head map
+    w2 = w.copy()
+    for pool in (w2.k_pool, w2.v_pool):
+        v = w2.pool_view(pool)
+        v[:, :, [0, 1]] = v[:, :, [1, 0]]
+    w2.k_scale = w.k_scale[[1, 0]].copy()
+    w2.v_scale = w.v_scale[[1, 0]].copy()
+    w2.head_map = 1 - w.head_map
+    assert np.array_equal(oracle.verify(w2), a)
+    # request 1 alone gives the same rows as in the batch
+    w3 = w.copy()
+    w3.batch = 1
+    w3.q_fp16 = w.q_fp16[1:].copy()
+    w3.block_table = w.block_table[1:].copy()
+    w3.live_len = w.live_len[1:].copy()
+    assert np.array_equal(oracle.verify(w3)[0], a[1])
+
+
+def test_pins_detect_planted_mistakes():
+    """Plant plausible mistakes (on the CPU, in the oracle's inputs so the
+    oracle computes exactly what a buggy oracle would) and check the SDPA pin
+    rejects every one of them at the tolerance the pins use."""
+    w = W.build(seed=14, batch=2, q=8, num_q_heads=8, num_kv_heads=2, head_dim=32, page_size=16, lengths=[120, 60])
+    ref = sdpa_reference(w)
+    assert _rel(oracle.verify(w), ref) < 1e-13
+    mutants = {}
+    m = w.copy(); m.live_len = m.live_len + 1
+    mutants["causal offset +1"] = oracle.verify(m)
+    mutants["scale 1/D instead of 1/sqrt(D)"] = oracle.verify(w, sm_scale=1.0 / w.head_dim)
+    m = w.copy(); m.k_pool, m.v_pool = w.v_pool, w.k_pool; m.k_scale, m.v_scale = w.v_scale, w.k_scale
+    mutants["K and V swapped"] = oracle.verify(m)
+    m = w.copy(); m.head_map = (np.arange(8) % 2).astype(np.int32)
+    mutants["head map h % Hkv"] = oracle.verify(m)
+    m = w.copy(); m.k_scale = np.ones_like(w.k_scale)
+    mutants["k_scale dropped"] = oracle.verify(m)
+    m = w.copy(); m.v_scale = np.ones_like(w.v_scale)
+    mutants["v_scale dropped"] = oracle.verify(m)
+    for name, out in mutants.items():
+        assert not (_rel(out, ref) <= 1e-3), name  # NaN (a read past the live range) also fails the pin
+
+
+# ------------------------------------------------------------- golden data --
+
+def test_golden_workspace_growth():
+    g = json.load(open(os.path.join(GOLDEN, "workspace_growth.json")))
+    lse = int(np.prod(g["lse_shape"])) * 4
+    ms = int(np.prod(g["max_sum_shape"])) * 4
+    assert ms - lse == g["growth_bytes"] == 15 * 1024
+    assert g["lse_shape"] == [g["splits"], g["q"], g["group"]]
+
+
+def test_golden_page_sizes_are_multiples_of_16():
+    g = json.load(open(os.path.join(GOLDEN, "page_sizes.json")))
+    assert all(p % 16 == 0 for p in g["page_sizes"])
+
+
+def test_golden_stride_counterexample_arithmetic():
+    g = json.load(open(os.path.join(GOLDEN, "stride_counterexample.json")))
+    pages, page, heads, dim = g["shape"]
+    s_page, s_tok, s_head, s_d = g["strides_bytes"]
+    assert s_page == page * s_tok and s_head == dim and s_d == 1
+    assert s_tok % 8 == 0 and s_tok % 16 != 0
+    assert g["second_token_first_byte"] == s_tok
+    assert (s_tok // 16) * 16 == g["paired_loader_would_read_from"]
