@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of one verify step (split kernel + combine kernel) on one MI355X.
+
+Default workload: batch 1, live length 261,888 + 256 = 262,144 tokens with the
+q = 8 verify rows at the end, 16 query heads / 2 KV heads, head_dim 256,
+E4M3 K/V with per-head scales and 1% outlier tokens, page size 64 (the
+256K-context q8 case the metric is quoted on). Inputs are synthetic, seeded and
+resident in HBM before the timed region starts.
+
+Timing: W untimed warmup steps, then K timed steps. Before every timed step an
+untimed 1 GiB write evicts the 256 MB Infinity Cache, so the KV bytes come
+from HBM; each step is bracketed by HIP events recorded on the stream the
+kernels run on (split: e0 -> e1, combine: e1 -> e2). The whole timed loop is
+also bracketed by a device synchronize.
+
+Prints one JSON line. `value` is the achieved KV read rate: live K+V bytes of
+the step divided by the mean step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify-step us + achieved KV HBM GB/s (% peak), q8 E4M3 at 256K ctx"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published
+KERNEL_SRC = os.path.join(ROOT, "paged_fp8_split_amd", "csrc", "pfs_kernels.hip")
+
+
+def note(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(cfg: int):
+    """HBM bytes per split-kernel launch measured with rocprofv3 PMC counters
+    (profiles/traffic_split_config<cfg>.json), if those counters were taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_split_config{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def split_algorithmic_bytes(w, plan) -> int:
+    """Bytes the split kernel must move: live K+V, Q, the block-table entries of
+    the live pages, and the FP32 partials (max, sum, D accumulators per row) of
+    every split that holds live tokens."""
+    import numpy as np
+
+    L = np.clip(w.live_len.astype(np.int64), 0, w.capacity)
+    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2
+    qb = w.batch * w.q * w.num_q_heads * w.head_dim * 2
+    bt = int((-(-L // w.page_size)).sum()) * 4
+    rows = w.q * w.group
+    splits = int((-(-L // plan.tokens_per_split)).sum())
+    ws = splits * w.num_kv_heads * rows * (w.head_dim + 2) * 4
+    return kv + qb + bt + ws
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """The FP64 oracle, as it stands, on the host cores: whole verify steps of
+    the same workload, repeated until `seconds` have elapsed (at least one)."""
+    import oracle
+
+    threads = oracle.max_threads()
+    units = w.batch * w.num_q_heads * w.q
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.verify(w)
+        reps += 1
+        el = time.perf_counter() - t0
+        note(f"cpu oracle step {reps}: {el:.1f} s elapsed")
+        if el >= seconds:
+            break
+    per_step = el / reps
+    return {
+        "value": round(w.kv_bytes() / per_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(min(threads, units)),
+        "kind": "oracle",
+        "sample": f"{reps} whole verify step(s) of the timed workload ({w.name}), FP64, "
+                  f"{per_step:.2f} s per step",
+        "seconds_per_step": round(per_step, 4),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="named workload (default 3: 256K context, q8)")
+    ap.add_argument("--tokens-per-split", type=int, default=0)
+    ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "this build measures the single-GPU verify step only (no collectives, no sharding).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_fp8_split_amd as pfs
+    from paged_fp8_split_amd import _lib
+    from paged_fp8_split_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    note(f"generating workload config {args.config}")
+    w = W.config(args.config)
+    t = W.device_tensors(w, dev)
+    plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
+                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"],
+                         tokens_per_split=args.tokens_per_split)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["q"])
+    scrub = None if args.no_scrub else torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream(dev)
+
+    def split():
+        _lib.verify_split(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["block_table"], t["live_len"], ws,
+                          stream)
+
+    def combine():
+        _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
+
+    note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B")
+    for _ in range(args.warmup):
+        if scrub is not None:
+            scrub.add_(1.0)
+        split()
+        combine()
+    torch.cuda.synchronize()
+    note("warmup done; timing")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if scrub is not None:
+            scrub.add_(1.0)
+        evs[k][0].record(stream)
+        split()
+        evs[k][1].record(stream)
+        combine()
+        evs[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    y = out.cpu().numpy()
+    out_sha = hashlib.sha256(y.tobytes()).hexdigest()
+
+    # the same step as one HIP graph, replayed back to back (cache-warm: context only)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _lib.verify(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
+                    t["live_len"], out, ws)
+    g.replay()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 50
+    ga.record()
+    for _ in range(reps):
+        g.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph_warm_ms = ga.elapsed_time(gb) / reps
+    same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
+
+    kv = w.kv_bytes()
+    mean_ms = float(step_ms.mean())
+    value = kv / (mean_ms * 1e-3) / 1e9
+    split_bytes = split_algorithmic_bytes(w, plan)
+    split_mean_ms = float(split_ms.mean())
+    achieved = split_bytes / (split_mean_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(args.config)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "us_per_step": round(mean_ms * 1e3, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "kv_pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "precision": "E4M3 KV bytes, FP16 MFMA operands, FP32 accumulation and split partials, FP16 output",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "context": int(w.live_len.max()),
+            "q": w.q,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "page_size": w.page_size,
+            "partition_tokens": 64,
+            "tokens_per_split": plan.tokens_per_split,
+            "num_splits": plan.num_splits,
+            "kv_bytes": kv,
+            "infinity_cache_scrub": scrub is not None,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pfs_split_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": split_bytes,
+            "mean_launch_us": round(split_mean_ms * 1e3, 2),
+        },
+        "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
+        "graph_replay_cache_warm_us": round(graph_warm_ms * 1e3, 2),
+        "graph_output_matches_eager": bool(same),
+        "timed_loop_wall_s": round(wall, 4),
+        "output_sha256": out_sha,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        note("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

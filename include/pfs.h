@@ -1,0 +1,187 @@
+/*
+ * pfs.h -- C ABI of libpfs: E4M3 paged speculative-verify attention with FP32
+ * split partials, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (defined by the pages "[Kernel][SM70] Add opt-in E4M3 grouped
+ * attention with FP32 partials", final-status section and Scope list, and
+ * "[Bugfix] Use FP32 state and E4M3 defaults for DFlash2", Purpose):
+ *
+ *   For request b, query head h (KV head g = head_map[h]) and draft row i in
+ *   [0, q): the row attends causally to the first n_i = clamp(L_b - q + i + 1,
+ *   0, L_b) tokens of the request's paged KV cache, where L_b = live_len[b]
+ *   counts the q draft tokens. K and V are stored as OCP E4M3 (FN) bytes with
+ *   one FP32 scale per KV head:  Khat = e4m3(k_byte) * k_scale[g],
+ *   Vhat = e4m3(v_byte) * v_scale[g].
+ *     s_j  = sm_scale * dot(Q[b,i,h,:], Khat_j)          for j < n_i
+ *     out  = sum_j exp(s_j - max s) Vhat_j / sum_j exp(s_j - max s)
+ *   rounded once to FP16 (round to nearest even). A row with n_i == 0
+ *   (retired request, or L_b < q) outputs +0.0.
+ *
+ *   The context is cut into splits of tokens_per_split tokens, each a run of
+ *   64-token partitions consumed in ascending order ("[Kernel] Finalize the
+ *   audited TP2 DFlash2 31/29 ms endpoint", Purpose: K64 partition order).
+ *   Every split emits an FP32 running max, an FP32 sum and an unnormalized
+ *   FP32 PV accumulator into the caller's workspace; a combine pass rescales
+ *   the splits, reduces them in ascending split order, normalizes and rounds
+ *   once ("... FP32 partials", revision 3 bullet: max/sum and unnormalized PV
+ *   kept in FP32 until one final combine).
+ *
+ * Every call returns a status code (PFS_OK == 0, errors < 0); no exception and
+ * no fallback path crosses this boundary: an unsupported shape is an error.
+ * The library never allocates, frees or synchronizes device memory; pfs_verify
+ * only enqueues kernels on the caller's stream and is safe to capture in a HIP
+ * graph.
+ */
+#ifndef PFS_H
+#define PFS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bumped whenever a signature, a struct layout or the numerics contract
+ * changes. Callers refuse a library whose pfs_abi_version() differs from the
+ * header they were built against (the pages' "stale native rejection":
+ * "[Bugfix] Use FP32 state ...", Purpose, precision revision / rebuild). */
+#define PFS_ABI_VERSION 1
+
+enum {
+    PFS_OK = 0,
+    PFS_ERR_NULL = -1,        /* a required pointer is NULL */
+    PFS_ERR_SHAPE = -2,       /* an inconsistent or out-of-range size/stride */
+    PFS_ERR_UNSUPPORTED = -3, /* head_dim, q, page size or partition not supported */
+    PFS_ERR_ALIGNMENT = -4,   /* a stride or a base pointer is not 16-byte aligned */
+    PFS_ERR_HEAD_MAP = -5,    /* head map entry out of range or groups not uniform */
+    PFS_ERR_WORKSPACE = -6,   /* workspace NULL, misaligned or smaller than required */
+    PFS_ERR_LAUNCH = -7,      /* the HIP runtime reported an error at launch */
+    PFS_ERR_NOMEM = -8        /* host allocation of the plan failed */
+};
+
+/* Opaque HIP stream handle (hipStream_t); NULL is the default stream. */
+typedef struct ihipStream_t* pfs_stream_t;
+
+/*
+ * Static description of one problem shape. Everything a plan depends on is in
+ * here; device data (pointers, live lengths, block-table contents) is not.
+ *
+ * KV pools: byte arrays addressed as
+ *   page * kv_page_stride + slot * kv_token_stride + kv_head * kv_head_stride + d
+ * for page in [0, num_pool_pages), slot in [0, page_size), d in [0, head_dim)
+ * (the pages' [num_blocks, block_size, kv_heads, head_dim] uint8 layout with
+ * byte strides; "... FP32 partials", AI integration review). The head_dim
+ * bytes of one (page, slot, kv_head) are contiguous. K and V pools share the
+ * same strides.
+ *
+ * Q and out: contiguous [batch, q, num_q_heads, head_dim] FP16.
+ */
+typedef struct pfs_problem {
+    int32_t batch;              /* requests, >= 0 (0: pfs_verify does nothing) */
+    int32_t q;                  /* draft rows per request, 1..16 */
+    int32_t num_q_heads;        /* multiple of num_kv_heads, <= 256 */
+    int32_t num_kv_heads;       /* >= 1 */
+    int32_t head_dim;           /* 64, 128 or 256 */
+    int32_t page_size;          /* tokens per page, a positive multiple of 16 */
+    int32_t max_pages_per_row;  /* block-table row length (capacity = this * page_size) */
+    int32_t num_pool_pages;     /* physical pages in each pool */
+    int32_t partition_tokens;   /* 64 (the only partition size this build runs) */
+    int32_t tokens_per_split;   /* 0 = library default; else a multiple of partition_tokens */
+    int64_t kv_page_stride;     /* bytes, multiple of 16 */
+    int64_t kv_token_stride;    /* bytes, multiple of 16 */
+    int64_t kv_head_stride;     /* bytes, multiple of 16, >= head_dim */
+    float sm_scale;             /* softmax scale, finite and > 0 (usually 1/sqrt(head_dim)) */
+    const int32_t* q_head_to_kv_head; /* HOST array [num_q_heads]; copied at plan time */
+} pfs_problem;
+
+typedef struct pfs_plan pfs_plan;
+
+/* The PFS_ABI_VERSION the library was built with. */
+int32_t pfs_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* pfs_status_string(int32_t status);
+
+/*
+ * Validate a problem and build a plan (host only: no HIP call, no device
+ * needed). On success *out owns a plan the caller releases with
+ * pfs_plan_destroy. Checks (each with its own status code): sizes and ranges,
+ * head_dim / q / page size / partition support, 16-byte stride alignment
+ * (the pages' counterexample, token stride 264 with a 16-byte paired loader,
+ * is rejected here with PFS_ERR_ALIGNMENT), non-overlapping nesting of the
+ * strides, and a uniform head map (every KV head serves exactly
+ * num_q_heads / num_kv_heads query heads).
+ * The plan is immutable and may be shared by host threads.
+ */
+int32_t pfs_plan_create(const pfs_problem* problem, pfs_plan** out);
+
+void pfs_plan_destroy(pfs_plan* plan);
+
+/* Bytes of device workspace pfs_verify needs for this plan (> 0). */
+int64_t pfs_plan_workspace_bytes(const pfs_plan* plan);
+
+/* Splits per request and tokens per split chosen by the plan. */
+int32_t pfs_plan_num_splits(const pfs_plan* plan);
+int32_t pfs_plan_tokens_per_split(const pfs_plan* plan);
+
+/*
+ * Enqueue one verify-attention step on `stream`.
+ *   q_fp16       device [batch, q, num_q_heads, head_dim] FP16, 16-byte aligned
+ *   k_pool/v_pool device byte pools (layout above), 16-byte aligned
+ *   k_scale/v_scale device [num_kv_heads] FP32 (read on device)
+ *   block_table  device [batch, max_pages_per_row] int32
+ *   live_len     device [batch] int32, draft tokens included
+ *   out_fp16     device [batch, q, num_q_heads, head_dim] FP16, 16-byte aligned
+ *   workspace    device scratch of at least pfs_plan_workspace_bytes(plan)
+ *                bytes, 256-byte aligned. Its contents need no initialization
+ *                and are overwritten; one workspace serves one in-flight call
+ *                at a time (stream order).
+ * Device-side preconditions (not checked on the host, which must not
+ * synchronize): live_len values are clamped into [0, capacity]; block-table
+ * entries are read only for logical pages below ceil(L_b / page_size) and
+ * must lie in [0, num_pool_pages); live K/V bytes are finite E4M3 codes
+ * (bytes no live token owns may hold anything, NaN codes included).
+ * All buffers are caller-owned. Returns PFS_OK or an error status; a launch
+ * error is reported as PFS_ERR_LAUNCH.
+ */
+int32_t pfs_verify(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool,
+                   const uint8_t* v_pool, const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, const int32_t* live_len, void* out_fp16,
+                   void* workspace, int64_t workspace_bytes, pfs_stream_t stream);
+
+/*
+ * The two phases of pfs_verify, for callers that time or schedule them apart.
+ * pfs_verify_split runs the split kernel (dequant-on-load, QK^T, online
+ * softmax, PV) and leaves every split's FP32 (max, sum, unnormalized PV) in
+ * the workspace; pfs_verify_combine reads those partials, rescales them, sums
+ * them in ascending split order, normalizes and writes the FP16 output.
+ * pfs_verify_split followed by pfs_verify_combine on the same stream, plan and
+ * workspace is exactly pfs_verify. Arguments and errors as for pfs_verify.
+ */
+int32_t pfs_verify_split(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool,
+                         const uint8_t* v_pool, const float* k_scale, const int32_t* block_table,
+                         const int32_t* live_len, void* workspace, int64_t workspace_bytes,
+                         pfs_stream_t stream);
+int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int32_t* live_len,
+                           void* out_fp16, const void* workspace, int64_t workspace_bytes,
+                           pfs_stream_t stream);
+
+/*
+ * E4M3 paged -> FP16 bridge (the dequant-on-load path exposed on its own;
+ * "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+ * Scope list: an explicit E4M3 paged-to-FP16 bridge API).
+ * Writes out_fp16 as a dense device array [batch, capacity, num_kv_heads,
+ * head_dim] (capacity = max_pages_per_row * page_size): element (b, t, g, d)
+ * is the exact FP16 value of the pool byte of token t of request b when
+ * t < live_len[b], and +0.0 otherwise. Every finite E4M3 value is an FP16
+ * normal number or zero, so the conversion is exact; NaN codes give NaN.
+ * Same alignment and precondition rules as pfs_verify; no workspace.
+ */
+int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
+                          const int32_t* live_len, void* out_fp16, pfs_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFS_H */

@@ -1,0 +1,112 @@
+"""paged_fp8_split_amd: E4M3 paged speculative-verify attention with FP32 split
+partials on AMD Instinct MI355X (gfx950).
+
+The hot path is the C-ABI library ``libpfs.so`` (include/pfs.h), built by
+``python -m paged_fp8_split_amd.build``. This package is its thin Python
+binding: it derives shapes and byte strides from torch tensors, caches plans
+and passes raw device pointers and the current HIP stream. Torch provides
+device memory and streams only; all arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+__all__ = ["verify", "dequant_paged", "make_plan", "Plan", "PfsError", "ABI_VERSION"]
+
+_plans: Dict[Tuple, "Plan"] = {}
+
+
+def __getattr__(name):
+    if name in ("Plan", "PfsError", "ABI_VERSION"):
+        from . import _lib
+
+        return getattr(_lib, name)
+    raise AttributeError(name)
+
+
+def _pool_layout(pool):
+    if pool.dtype.itemsize != 1 or pool.dim() != 4:
+        raise ValueError("KV pools must be uint8 tensors shaped [pages, page_size, kv_heads, head_dim]")
+    if pool.stride(3) != 1:
+        raise ValueError("the head_dim bytes of a KV pool must be contiguous")
+    pages, page, hkv, d = pool.shape
+    return int(pages), int(page), int(hkv), int(d), tuple(int(s) for s in pool.stride()[:3])
+
+
+def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_scale=None,
+              partition_tokens=64, tokens_per_split=0):
+    """Plan (cached) for a problem whose KV pools look like ``k_pool``."""
+    from . import _lib
+
+    pages, page, hkv, d, (sp, st, sh) = _pool_layout(k_pool)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    hm = tuple(int(x) for x in head_map)
+    key = (batch, q, num_q_heads, hkv, d, page, max_pages_per_row, pages, sp, st, sh, float(sm_scale), hm,
+           partition_tokens, tokens_per_split)
+    plan = _plans.get(key)
+    if plan is None:
+        plan = _lib.Plan(batch=batch, q=q, num_q_heads=num_q_heads, num_kv_heads=hkv, head_dim=d, page_size=page,
+                         max_pages_per_row=max_pages_per_row, num_pool_pages=pages, kv_page_stride=sp,
+                         kv_token_stride=st, kv_head_stride=sh, sm_scale=sm_scale, head_map=hm,
+                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split)
+        _plans[key] = plan
+    return plan
+
+
+def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_map: Optional[Sequence[int]] = None,
+           sm_scale: Optional[float] = None, partition_tokens: int = 64, tokens_per_split: int = 0, out=None,
+           workspace=None, stream=None, plan=None):
+    """Verify attention of q draft rows per request over a paged E4M3 KV cache.
+
+    q            [B, q, Hq, D] float16, contiguous, on the GPU
+    k_pool/v_pool [pages, page_size, Hkv, D] uint8 (E4M3 bytes), head_dim
+                 contiguous, identical strides (multiples of 16 bytes)
+    k_scale/v_scale [Hkv] float32
+    block_table  [B, max_pages_per_row] int32
+    live_len     [B] int32, draft tokens included
+    head_map     query head -> KV head (default h // (Hq // Hkv))
+    Returns out [B, q, Hq, D] float16. No host synchronization.
+    """
+    from . import _lib
+    import torch
+
+    B, nq, Hq, D = (int(x) for x in q.shape)
+    if q.dtype != torch.float16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16 tensor [B, q, Hq, D]")
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("K and V pools must share shape and strides")
+    hkv = int(k_pool.shape[2])
+    if head_map is None:
+        head_map = [h // (Hq // hkv) for h in range(Hq)] if Hq % hkv == 0 else list(range(Hq))
+    if plan is None:
+        plan = make_plan(batch=B, q=nq, num_q_heads=Hq, head_map=head_map, k_pool=k_pool,
+                         max_pages_per_row=int(block_table.shape[1]), sm_scale=sm_scale,
+                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split)
+    for name, t, dt in (("k_scale", k_scale, torch.float32), ("v_scale", v_scale, torch.float32),
+                        ("block_table", block_table, torch.int32), ("live_len", live_len, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    _lib.verify(plan, q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, out, workspace, stream)
+    return out
+
+
+def dequant_paged(pool, block_table, live_len, *, out=None, stream=None):
+    """Paged E4M3 pool -> dense float16 [B, capacity, Hkv, D]; tokens at or
+    beyond a request's live length are +0.0."""
+    from . import _lib
+    import torch
+
+    pages, page, hkv, d, _ = _pool_layout(pool)
+    B = int(block_table.shape[0])
+    plan = make_plan(batch=B, q=1, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=pool,
+                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0)
+    if out is None:
+        out = torch.empty((B, plan.capacity, hkv, d), dtype=torch.float16, device=pool.device)
+    _lib.dequant_paged(plan, pool, block_table, live_len, out, stream)
+    return out

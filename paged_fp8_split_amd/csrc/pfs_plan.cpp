@@ -1,0 +1,228 @@
+// pfs_plan.cpp -- host side of libpfs: ABI version, status strings, problem
+// validation, split planning and workspace sizing. No HIP call is made here,
+// so every check runs (and is tested) on a machine without a GPU.
+#include <limits.h>
+#include <math.h>
+#include <new>
+#include <stdint.h>
+#include <string.h>
+
+#include "pfs_internal.h"
+
+namespace {
+
+bool is_multiple(int64_t v, int64_t m) { return v % m == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Row tiles (of 16 rows) per split workgroup: the smallest supported tile count
+// that holds all rows, capped by the accumulator budget; the rest becomes row
+// blocks along the grid.
+void choose_row_tiles(int32_t rows, int32_t head_dim, int32_t* tiles, int32_t* blocks) {
+    const int32_t max_tiles = pfs::kMaxRowsTimesDim / (16 * head_dim);  // 4, 8 or 16
+    static const int32_t kTiles[] = {1, 2, 4, 8, 16};
+    int32_t need = (rows + 15) / 16;
+    if (need > max_tiles) {
+        *tiles = max_tiles;
+        *blocks = (rows + 16 * max_tiles - 1) / (16 * max_tiles);
+        return;
+    }
+    for (int32_t t : kTiles) {
+        if (t >= need) {
+            *tiles = t;
+            break;
+        }
+    }
+    *blocks = 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pfs_abi_version(void) { return PFS_ABI_VERSION; }
+
+const char* pfs_status_string(int32_t status) {
+    switch (status) {
+        case PFS_OK: return "ok";
+        case PFS_ERR_NULL: return "a required pointer is NULL";
+        case PFS_ERR_SHAPE: return "inconsistent or out-of-range size or stride";
+        case PFS_ERR_UNSUPPORTED: return "unsupported head_dim, q, page size or partition size";
+        case PFS_ERR_ALIGNMENT: return "a KV stride or a base pointer is not 16-byte aligned";
+        case PFS_ERR_HEAD_MAP: return "head map entry out of range or KV-head groups not uniform";
+        case PFS_ERR_WORKSPACE: return "workspace NULL, misaligned (256 B) or too small";
+        case PFS_ERR_LAUNCH: return "HIP kernel launch failed";
+        case PFS_ERR_NOMEM: return "host allocation failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
+    if (!pr || !out) return PFS_ERR_NULL;
+    *out = nullptr;
+    const pfs_problem& p = *pr;
+    if (!p.q_head_to_kv_head) return PFS_ERR_NULL;
+
+    // sizes and ranges
+    if (p.batch < 0 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.page_size < 1 ||
+        p.max_pages_per_row < 1 || p.num_pool_pages < 1)
+        return PFS_ERR_SHAPE;
+    if (p.num_q_heads > pfs::kMaxQHeads || p.num_q_heads % p.num_kv_heads != 0) return PFS_ERR_SHAPE;
+    if (p.batch > 65535) return PFS_ERR_SHAPE;  // grid z
+    if (!(p.sm_scale > 0.0f) || !isfinite(p.sm_scale)) return PFS_ERR_SHAPE;
+    const int64_t capacity = (int64_t)p.max_pages_per_row * p.page_size;
+    if (capacity > (int64_t)INT32_MAX / 2) return PFS_ERR_SHAPE;
+
+    // what the kernels run
+    if (p.q < 1 || p.q > pfs::kMaxQ) return PFS_ERR_UNSUPPORTED;
+    if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256) return PFS_ERR_UNSUPPORTED;
+    if (p.page_size % 16 != 0) return PFS_ERR_UNSUPPORTED;
+    if (p.partition_tokens != pfs::kPartitionTokens) return PFS_ERR_UNSUPPORTED;
+    if (p.tokens_per_split < 0 || !is_multiple(p.tokens_per_split, p.partition_tokens))
+        return PFS_ERR_SHAPE;
+
+    // strides: 16-byte units (the loads are 16 bytes wide), then nesting
+    if (p.kv_head_stride <= 0 || p.kv_token_stride <= 0 || p.kv_page_stride <= 0) return PFS_ERR_SHAPE;
+    if (!is_multiple(p.kv_head_stride, 16) || !is_multiple(p.kv_token_stride, 16) ||
+        !is_multiple(p.kv_page_stride, 16))
+        return PFS_ERR_ALIGNMENT;
+    const int64_t head_span = (int64_t)(p.num_kv_heads - 1) * p.kv_head_stride + p.head_dim;
+    if (p.kv_head_stride < p.head_dim) return PFS_ERR_SHAPE;
+    if (p.kv_token_stride < head_span) return PFS_ERR_SHAPE;
+    if (p.kv_page_stride < (int64_t)(p.page_size - 1) * p.kv_token_stride + head_span) return PFS_ERR_SHAPE;
+    if ((double)p.kv_page_stride * (double)p.num_pool_pages > 4.0e18) return PFS_ERR_SHAPE;
+
+    // head map: in range and uniform groups
+    const int32_t G = p.num_q_heads / p.num_kv_heads;
+    int32_t count[pfs::kMaxQHeads] = {0};
+    for (int32_t h = 0; h < p.num_q_heads; ++h) {
+        const int32_t g = p.q_head_to_kv_head[h];
+        if (g < 0 || g >= p.num_kv_heads) return PFS_ERR_HEAD_MAP;
+        count[g]++;
+    }
+    for (int32_t g = 0; g < p.num_kv_heads; ++g)
+        if (count[g] != G) return PFS_ERR_HEAD_MAP;
+
+    pfs_plan* plan = new (std::nothrow) pfs_plan;
+    if (!plan) return PFS_ERR_NOMEM;
+    memset(plan, 0, sizeof(*plan));
+    plan->p = p;
+    plan->p.q_head_to_kv_head = nullptr;
+    plan->group = G;
+    plan->rows = G * p.q;
+    plan->capacity = (int32_t)capacity;
+    {
+        int32_t fill[pfs::kMaxQHeads] = {0};
+        for (int32_t h = 0; h < p.num_q_heads; ++h) {
+            const int32_t g = p.q_head_to_kv_head[h];
+            plan->qhead[g * G + fill[g]++] = (uint8_t)h;
+        }
+    }
+    choose_row_tiles(plan->rows, p.head_dim, &plan->row_tiles, &plan->row_blocks);
+
+    // Split length: a pure function of the shape (never of device data), so a
+    // plan always folds the same partitions in the same order.
+    int64_t tps = p.tokens_per_split;
+    if (tps == 0) {
+        const int64_t units = (int64_t)(p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->row_blocks;
+        int64_t splits = (pfs::kDefaultTargetWorkgroups + units - 1) / units;
+        if (splits < 1) splits = 1;
+        tps = round_up((capacity + splits - 1) / splits, pfs::kPartitionTokens);
+        const int64_t min_tps = (int64_t)pfs::kWaves * pfs::kPartitionTokens;  // one partition per wave
+        if (tps < min_tps) tps = min_tps;
+    }
+    if (tps > round_up(capacity, pfs::kPartitionTokens)) tps = round_up(capacity, pfs::kPartitionTokens);
+    plan->tokens_per_split = (int32_t)tps;
+    plan->num_splits = (int32_t)((capacity + tps - 1) / tps);
+
+    const int64_t slots = (int64_t)plan->num_splits * (p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->rows;
+    plan->ws_ml_offset = 0;
+    plan->ws_acc_offset = round_up(slots * 2 * (int64_t)sizeof(float), 256);
+    plan->ws_bytes = plan->ws_acc_offset + round_up(slots * p.head_dim * (int64_t)sizeof(float), 256);
+    *out = plan;
+    return PFS_OK;
+}
+
+void pfs_plan_destroy(pfs_plan* plan) { delete plan; }
+
+int64_t pfs_plan_workspace_bytes(const pfs_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+int32_t pfs_plan_num_splits(const pfs_plan* plan) { return plan ? plan->num_splits : 0; }
+
+int32_t pfs_plan_tokens_per_split(const pfs_plan* plan) { return plan ? plan->tokens_per_split : 0; }
+
+namespace {
+
+bool misaligned16(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+bool misaligned4(const void* p) { return ((uintptr_t)p & 3u) != 0; }
+
+int32_t check_workspace(const pfs_plan* plan, const void* workspace, int64_t workspace_bytes) {
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < plan->ws_bytes) return PFS_ERR_WORKSPACE;
+    return PFS_OK;
+}
+
+int32_t check_split_args(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const float* k_scale, const int32_t* block_table, const int32_t* live_len,
+                         const void* workspace, int64_t workspace_bytes) {
+    if (!q_fp16 || !k_pool || !v_pool || !k_scale || !block_table || !live_len) return PFS_ERR_NULL;
+    if (misaligned16(q_fp16) || misaligned16(k_pool) || misaligned16(v_pool)) return PFS_ERR_ALIGNMENT;
+    if (misaligned4(k_scale) || misaligned4(block_table) || misaligned4(live_len)) return PFS_ERR_ALIGNMENT;
+    return check_workspace(plan, workspace, workspace_bytes);
+}
+
+int32_t check_combine_args(const pfs_plan* plan, const float* v_scale, const int32_t* live_len, const void* out_fp16,
+                           const void* workspace, int64_t workspace_bytes) {
+    if (!v_scale || !live_len || !out_fp16) return PFS_ERR_NULL;
+    if (misaligned16(out_fp16)) return PFS_ERR_ALIGNMENT;
+    if (misaligned4(v_scale) || misaligned4(live_len)) return PFS_ERR_ALIGNMENT;
+    return check_workspace(plan, workspace, workspace_bytes);
+}
+
+}  // namespace
+
+int32_t pfs_verify(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool, const uint8_t* v_pool,
+                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                   const int32_t* live_len, void* out_fp16, void* workspace, int64_t workspace_bytes,
+                   pfs_stream_t stream) {
+    if (!plan) return PFS_ERR_NULL;
+    if (plan->p.batch == 0) return PFS_OK;
+    int32_t st = check_split_args(plan, q_fp16, k_pool, v_pool, k_scale, block_table, live_len, workspace,
+                                  workspace_bytes);
+    if (st == PFS_OK) st = check_combine_args(plan, v_scale, live_len, out_fp16, workspace, workspace_bytes);
+    if (st != PFS_OK) return st;
+    st = pfs_launch_split(plan, q_fp16, k_pool, v_pool, k_scale, block_table, live_len, workspace, stream);
+    if (st != PFS_OK) return st;
+    return pfs_launch_combine(plan, v_scale, live_len, out_fp16, workspace, stream);
+}
+
+int32_t pfs_verify_split(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const float* k_scale, const int32_t* block_table, const int32_t* live_len,
+                         void* workspace, int64_t workspace_bytes, pfs_stream_t stream) {
+    if (!plan) return PFS_ERR_NULL;
+    if (plan->p.batch == 0) return PFS_OK;
+    const int32_t st = check_split_args(plan, q_fp16, k_pool, v_pool, k_scale, block_table, live_len, workspace,
+                                        workspace_bytes);
+    if (st != PFS_OK) return st;
+    return pfs_launch_split(plan, q_fp16, k_pool, v_pool, k_scale, block_table, live_len, workspace, stream);
+}
+
+int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int32_t* live_len, void* out_fp16,
+                           const void* workspace, int64_t workspace_bytes, pfs_stream_t stream) {
+    if (!plan) return PFS_ERR_NULL;
+    if (plan->p.batch == 0) return PFS_OK;
+    const int32_t st = check_combine_args(plan, v_scale, live_len, out_fp16, workspace, workspace_bytes);
+    if (st != PFS_OK) return st;
+    return pfs_launch_combine(plan, v_scale, live_len, out_fp16, workspace, stream);
+}
+
+int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
+                          const int32_t* live_len, void* out_fp16, pfs_stream_t stream) {
+    if (!plan) return PFS_ERR_NULL;
+    if (plan->p.batch == 0) return PFS_OK;
+    if (!pool || !block_table || !live_len || !out_fp16) return PFS_ERR_NULL;
+    if (((uintptr_t)pool | (uintptr_t)out_fp16) & 15u) return PFS_ERR_ALIGNMENT;
+    if (((uintptr_t)block_table | (uintptr_t)live_len) & 3u) return PFS_ERR_ALIGNMENT;
+    return pfs_launch_dequant(plan, pool, block_table, live_len, out_fp16, stream);
+}
+
+}  // extern "C"

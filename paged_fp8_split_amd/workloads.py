@@ -353,3 +353,27 @@ def config(cfg: int, *, q: Optional[int] = None, seed: Optional[int] = None, **o
         kw["q"] = q
     kw.update(overrides)
     return build(seed=seed, **kw)
+
+
+def device_tensors(w: Workload, device) -> dict:
+    """Copy a workload to ``device`` as the torch tensors the binding takes.
+    The pools become [pages, page_size, Hkv, D] uint8 views with the
+    workload's byte strides over one flat allocation each."""
+    import torch
+
+    def pool(flat):
+        t = torch.from_numpy(flat).to(device)
+        return t.as_strided((w.num_pool_pages, w.page_size, w.num_kv_heads, w.head_dim),
+                            (w.page_stride, w.token_stride, w.head_stride, 1))
+
+    return {
+        "q": torch.from_numpy(np.ascontiguousarray(w.q_fp16)).to(device),
+        "k_pool": pool(w.k_pool),
+        "v_pool": pool(w.v_pool),
+        "k_scale": torch.from_numpy(w.k_scale.copy()).to(device),
+        "v_scale": torch.from_numpy(w.v_scale.copy()).to(device),
+        "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table)).to(device),
+        "live_len": torch.from_numpy(w.live_len.copy()).to(device),
+        "head_map": [int(x) for x in w.head_map],
+        "sm_scale": float(w.sm_scale),
+    }

@@ -1,0 +1,81 @@
+"""Shared helpers of the GPU tests: run the HIP path on a workload and judge
+its FP16 output against the FP64 oracle."""
+from __future__ import annotations
+
+import hashlib
+import sys
+
+import numpy as np
+
+import oracle
+import paged_fp8_split_amd as pfs
+from paged_fp8_split_amd import workloads as W
+
+REL_L2_TOL = 1e-3   # relative L2 over every output element of the launch
+MAX_ABS_TOL = 4e-3  # max |y - r| on elements with |r| < 8
+# On |r| >= 8 no FP16 value can be within 4e-3 of every real number (half an
+# FP16 ulp there is >= 2^-8 = 3.9e-3), so those elements are held to one FP16
+# ulp of r (faithful rounding) instead.
+LARGE = 8.0
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def device():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def run(w: W.Workload, *, tokens_per_split: int = 0, tensors=None, out=None, workspace=None, stream=None):
+    """HIP verify on workload w; returns (out tensor, tensors dict)."""
+    dev = device()
+    t = tensors if tensors is not None else W.device_tensors(w, dev)
+    o = pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
+                   head_map=t["head_map"], sm_scale=t["sm_scale"], tokens_per_split=tokens_per_split, out=out,
+                   workspace=workspace, stream=stream)
+    return o, t
+
+
+def to_np(out) -> np.ndarray:
+    import torch
+
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def fp16_ulp(r: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(r), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(a)) - 10)
+
+
+def judge(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
+    """Parity of GPU FP16 output y16 with the unrounded oracle result r."""
+    y = y16.astype(np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output"
+    err = np.abs(y - r)
+    rel = float(np.linalg.norm(err.ravel()) / max(np.linalg.norm(r.ravel()), 1e-300))
+    small = np.abs(r) < LARGE
+    max_abs_small = float(err[small].max()) if small.any() else 0.0
+    max_ulps_large = float((err[~small] / fp16_ulp(r[~small])).max()) if (~small).any() else 0.0
+    rne = r.astype(np.float16)
+    disagree = int((y16.view(np.uint16) != rne.view(np.uint16)).sum())
+    rep = dict(rel_l2=rel, max_abs=float(err.max()), max_abs_small=max_abs_small, max_ulps_large=max_ulps_large,
+               fp16_disagreements=disagree, elements=int(r.size))
+    log(f"[parity] {what}: {rep}")
+    assert rel <= REL_L2_TOL, f"{what}: rel L2 {rel}"
+    assert max_abs_small <= MAX_ABS_TOL, f"{what}: max abs {max_abs_small}"
+    assert max_ulps_large <= 1.0, f"{what}: {max_ulps_large} ulp on |r| >= 8"
+    return rep
+
+
+def sha(a) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def oracle_ref(w: W.Workload, **kw) -> np.ndarray:
+    return oracle.verify(w, **kw)

@@ -1,0 +1,178 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+symbol include/pfs.h declares, and rejects every invalid problem with its own
+status code before any HIP call is made."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from paged_fp8_split_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pfs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pfs_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = header_functions()
+    assert names == sorted([
+        "pfs_abi_version", "pfs_dequant_paged", "pfs_plan_create", "pfs_plan_destroy", "pfs_plan_num_splits",
+        "pfs_plan_tokens_per_split", "pfs_plan_workspace_bytes", "pfs_status_string", "pfs_verify",
+        "pfs_verify_combine", "pfs_verify_split"])
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.pfs_abi_version() == _lib.ABI_VERSION
+    for code, name in _lib.STATUS.items():
+        s = _lib.status_string(code)
+        assert s and s != "unknown status", name
+    assert _lib.status_string(12345) == "unknown status"
+
+
+def test_stale_library_is_refused():
+    class Stale:
+        @staticmethod
+        def pfs_abi_version():
+            return _lib.ABI_VERSION - 1
+
+    with pytest.raises(RuntimeError, match="does not match"):
+        _lib.check_abi(Stale())
+
+
+BASE = dict(batch=1, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64, max_pages_per_row=4096,
+            num_pool_pages=5000, kv_page_stride=64 * 512, kv_token_stride=512, kv_head_stride=256, sm_scale=0.0625,
+            head_map=[h // 8 for h in range(16)])
+
+
+def plan_status(**over):
+    kw = dict(BASE)
+    kw.update(over)
+    try:
+        _lib.Plan(**kw)
+        return 0
+    except _lib.PfsError as e:
+        return e.status
+
+
+def test_valid_problem_plans():
+    p = _lib.Plan(**BASE)
+    assert p.tokens_per_split % 64 == 0
+    assert p.num_splits * p.tokens_per_split >= p.capacity
+    assert p.workspace_bytes > 0
+    # planning is a pure function of the shape
+    q = _lib.Plan(**BASE)
+    assert (p.num_splits, p.tokens_per_split, p.workspace_bytes) == (q.num_splits, q.tokens_per_split,
+                                                                      q.workspace_bytes)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), "PFS_ERR_UNSUPPORTED"),
+    (dict(head_dim=512), "PFS_ERR_UNSUPPORTED"),
+    (dict(q=0), "PFS_ERR_UNSUPPORTED"),
+    (dict(q=17), "PFS_ERR_UNSUPPORTED"),
+    (dict(page_size=40, kv_page_stride=40 * 512), "PFS_ERR_UNSUPPORTED"),
+    (dict(partition_tokens=32), "PFS_ERR_UNSUPPORTED"),
+    (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
+    (dict(num_q_heads=15, head_map=[0] * 15), "PFS_ERR_SHAPE"),
+    (dict(batch=-1), "PFS_ERR_SHAPE"),
+    (dict(batch=65536), "PFS_ERR_SHAPE"),
+    (dict(sm_scale=0.0), "PFS_ERR_SHAPE"),
+    (dict(sm_scale=float("nan")), "PFS_ERR_SHAPE"),
+    (dict(kv_head_stride=128), "PFS_ERR_SHAPE"),             # heads overlap
+    (dict(kv_token_stride=496), "PFS_ERR_SHAPE"),            # tokens overlap
+    (dict(kv_page_stride=63 * 512), "PFS_ERR_SHAPE"),        # pages overlap
+    (dict(kv_token_stride=520, kv_page_stride=64 * 520), "PFS_ERR_ALIGNMENT"),
+    (dict(kv_page_stride=64 * 512 + 8), "PFS_ERR_ALIGNMENT"),
+    (dict(head_map=[0] * 16), "PFS_ERR_HEAD_MAP"),            # groups not uniform
+    (dict(head_map=[h // 8 for h in range(15)] + [2]), "PFS_ERR_HEAD_MAP"),  # out of range
+])
+def test_invalid_problems_are_rejected(over, status):
+    assert plan_status(**over) == _lib.STATUS_CODE[status]
+
+
+def test_pages_stride_counterexample_is_rejected():
+    g = json.load(open(os.path.join(GOLDEN, "stride_counterexample.json")))
+    pages, page, heads, dim = g["shape"]
+    sp, st, sh, _ = g["strides_bytes"]
+    s = plan_status(batch=1, q=5, num_q_heads=6, num_kv_heads=heads, head_dim=dim, page_size=page,
+                    max_pages_per_row=pages, num_pool_pages=pages, kv_page_stride=sp, kv_token_stride=st,
+                    kv_head_stride=sh, head_map=[0] * 6)
+    assert s == _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    # the same cache with the token stride padded to the next 16-byte unit is accepted
+    assert plan_status(batch=1, q=5, num_q_heads=6, num_kv_heads=heads, head_dim=dim, page_size=page,
+                       max_pages_per_row=pages, num_pool_pages=pages, kv_page_stride=page * 272,
+                       kv_token_stride=272, kv_head_stride=sh, head_map=[0] * 6) == 0
+
+
+def test_pages_page_sizes_are_accepted():
+    g = json.load(open(os.path.join(GOLDEN, "page_sizes.json")))
+    for page in g["page_sizes"]:
+        assert plan_status(page_size=page, kv_page_stride=page * 512, max_pages_per_row=2) == 0, page
+
+
+def test_workspace_holds_max_sum_pairs_per_split_row():
+    # the pages' workspace change: [80, 8, 6] log-sum-exp -> [80, 8, 6, 2] max/sum,
+    # i.e. 15 KiB more for 80 splits x q8 x GQA6 (one KV head per rank)
+    g = json.load(open(os.path.join(GOLDEN, "workspace_growth.json")))
+    S, q, G = g["splits"], g["q"], g["group"]
+    p = _lib.Plan(batch=1, q=q, num_q_heads=G, num_kv_heads=1, head_dim=256, page_size=64, max_pages_per_row=S,
+                  num_pool_pages=S, kv_page_stride=64 * 256, kv_token_stride=256, kv_head_stride=256,
+                  sm_scale=0.0625, head_map=[0] * G, tokens_per_split=64)
+    assert p.num_splits == S
+    ml = S * q * G * 2 * 4
+    assert ml - S * q * G * 4 == g["growth_bytes"]
+    acc = S * q * G * 256 * 4
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert p.workspace_bytes == rnd(ml) + rnd(acc)
+
+
+def test_verify_host_checks_need_no_device():
+    p = _lib.Plan(**BASE)
+    lib = _lib.load()
+    ok = 1 << 20  # any 256-aligned non-null address: these calls return before touching it
+    args = [ok] * 9
+    # NULL pointer
+    assert lib.pfs_verify(p.handle, None, *args[1:], p.workspace_bytes, None) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    # misaligned Q
+    bad = [ok + 8] + args[1:]
+    assert lib.pfs_verify(p.handle, *bad, p.workspace_bytes, None) == _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    # workspace too small, NULL or misaligned
+    assert lib.pfs_verify(p.handle, *args, p.workspace_bytes - 1, None) == _lib.STATUS_CODE["PFS_ERR_WORKSPACE"]
+    assert lib.pfs_verify(p.handle, *args[:8], None, p.workspace_bytes, None) == \
+        _lib.STATUS_CODE["PFS_ERR_WORKSPACE"]
+    assert lib.pfs_verify(p.handle, *args[:8], ok + 64, p.workspace_bytes, None) == \
+        _lib.STATUS_CODE["PFS_ERR_WORKSPACE"]
+    # a NULL plan
+    assert lib.pfs_verify(None, *args, p.workspace_bytes, None) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    # the two phases check the same things
+    assert lib.pfs_verify_split(p.handle, ok + 8, *([ok] * 7), p.workspace_bytes, None) == \
+        _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    assert lib.pfs_verify_split(p.handle, *([ok] * 8), p.workspace_bytes - 1, None) == \
+        _lib.STATUS_CODE["PFS_ERR_WORKSPACE"]
+    assert lib.pfs_verify_combine(p.handle, ok, ok, ok + 2, ok, p.workspace_bytes, None) == \
+        _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    assert lib.pfs_verify_combine(p.handle, None, ok, ok, ok, p.workspace_bytes, None) == \
+        _lib.STATUS_CODE["PFS_ERR_NULL"]
+    assert lib.pfs_plan_workspace_bytes(None) == 0
+    # an empty batch is a no-op that touches nothing
+    e = _lib.Plan(**dict(BASE, batch=0))
+    assert lib.pfs_verify(e.handle, *([None] * 9), 0, None) == 0
+
+
+def test_plan_create_null_arguments():
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    assert lib.pfs_plan_create(None, ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 64 * 512, 512, 256, 0.0625, None)
+    assert lib.pfs_plan_create(ctypes.byref(prob), ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]

@@ -1,0 +1,177 @@
+"""GPU parity of the HIP path against the FP64 oracle, small and medium shapes,
+plus the bitwise E4M3 dequant bridge. Everything goes through the C ABI."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_fp8_split_amd as pfs
+from paged_fp8_split_amd import workloads as W
+
+from parity import device, judge, log, oracle_ref, run, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _all_finite_codes(n):
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    return np.resize(codes, n)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_dequant_bridge_is_exact_on_every_finite_code(D):
+    import torch
+
+    w = W.build(seed=20 + D, batch=3, q=1, num_q_heads=2, num_kv_heads=2, head_dim=D, page_size=16,
+                lengths=[300, 77, 0], token_pad=16, page_pad=32)
+    log(f"[dequant] D={D} lengths={w.live_len.tolist()}")
+    view = w.pool_view(w.k_pool)
+    for b in range(w.batch):
+        L = int(w.live_len[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        n = L * w.num_kv_heads * D
+        view[w.block_table[b, t // 16], t % 16] = _all_finite_codes(n + 97 * b).reshape(-1)[-n:].reshape(L, 2, D)
+    t = W.device_tensors(w, device())
+    got = to_np(pfs.dequant_paged(t["k_pool"], t["block_table"], t["live_len"]))
+    table = oracle.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float16).numpy()
+    assert np.array_equal(table[~np.isnan(table)].astype(np.float16).view(np.uint16),
+                          ref[~np.isnan(table)].view(np.uint16))
+    cap = w.capacity
+    for b in range(w.batch):
+        L = int(w.live_len[b])
+        tt = np.arange(L)
+        raw = view[w.block_table[b, tt // 16], tt % 16]
+        exp = table[raw].astype(np.float16)
+        assert np.array_equal(got[b, :L].view(np.uint16), exp.view(np.uint16)), f"request {b}"
+        assert np.all(got[b, L:cap].view(np.uint16) == 0)
+
+
+SMALL = [
+    # (name, build kwargs, tokens_per_split)
+    ("d64-q8-g4-split64", dict(batch=1, q=8, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16,
+                               lengths=[1032]), 64),
+    ("d64-q8-g4-default", dict(batch=1, q=8, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=16,
+                               lengths=[1032]), 0),
+    ("d128-q1-g8-ragged", dict(batch=3, q=1, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
+                               lengths=[1000, 37, 513]), 256),
+    ("d128-q16-g8", dict(batch=2, q=16, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=32,
+                         lengths=[777, 16]), 256),
+    ("d256-q8-g8", dict(batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                        lengths=[2100, 300]), 512),
+    ("d256-q3-g2-short", dict(batch=4, q=3, num_q_heads=4, num_kv_heads=2, head_dim=256, page_size=16,
+                              lengths=[2, 0, 3, 130]), 0),
+    ("d64-q16-g16-rowblocks", dict(batch=1, q=16, num_q_heads=16, num_kv_heads=1, head_dim=64, page_size=16,
+                                   lengths=[600]), 256),
+    ("d256-q16-g8-rowblocks", dict(batch=1, q=16, num_q_heads=8, num_kv_heads=1, head_dim=256, page_size=64,
+                                   lengths=[700]), 256),
+    ("d128-q5-g6-padded", dict(batch=2, q=5, num_q_heads=12, num_kv_heads=2, head_dim=128, page_size=48,
+                               lengths=[400, 90], token_pad=16, page_pad=64), 0),
+    ("d64-outliers-pow2", dict(batch=2, q=8, num_q_heads=8, num_kv_heads=4, head_dim=64, page_size=16,
+                               lengths=[900, 333], outlier_frac=0.02, scale_mode="pow2",
+                               pow2_scale_exps=[-6, -3, 1, 4]), 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, kw, tps = case
+    w = W.build(seed=zlib.crc32(name.encode()) % 1000, **kw)
+    log(f"[small] {name} tps={tps}")
+    out, _ = run(w, tokens_per_split=tps)
+    judge(to_np(out), oracle_ref(w), name)
+
+
+def test_rows_without_visible_keys_are_positive_zero():
+    w = W.build(seed=31, batch=3, q=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                lengths=[0, 5, 40])
+    out = to_np(run(w)[0])
+    bits = out.view(np.uint16)
+    assert np.all(bits[0] == 0)           # retired request
+    assert np.all(bits[1, :3] == 0)       # rows that see nothing (L < q)
+    assert np.all(out[1, 3:] != 0)
+    judge(out, oracle_ref(w), "zero rows")
+
+
+def test_padded_strides_match_contiguous_bitwise():
+    kw = dict(batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64, lengths=[1500, 400])
+    a = W.build(seed=41, **kw)
+    variants = [W.build(seed=41, token_pad=16, **kw), W.build(seed=41, page_pad=16 * 7, **kw),
+                W.build(seed=41, token_pad=512, page_pad=256, **kw)]
+    ya = to_np(run(a)[0])
+    judge(ya, oracle_ref(a), "contiguous")
+    for v in variants:
+        yv = to_np(run(v)[0])
+        assert np.array_equal(ya.view(np.uint16), yv.view(np.uint16)), (v.token_stride, v.page_stride)
+
+
+def test_tail_sentinels_do_not_leak():
+    w = W.build(seed=42, batch=2, q=8, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=64,
+                lengths=[1000, 70])
+    a = to_np(run(W.set_tail_sentinel(w, W.SENTINEL_NAN))[0])
+    b = to_np(run(W.set_tail_sentinel(w, W.SENTINEL_MAX))[0])
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    judge(a, oracle_ref(w), "sentinels")
+
+
+def test_power_of_two_v_scale_is_exact():
+    w = W.build(seed=43, batch=1, q=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=64, lengths=[800])
+    a = to_np(run(w)[0]).astype(np.float64)
+    w2 = w.copy()
+    w2.v_scale = (w.v_scale * np.float32(4.0)).astype(np.float32)
+    b = to_np(run(w2)[0]).astype(np.float64)
+    # exact wherever both results are FP16 normal numbers (subnormal rounding
+    # is not scale invariant); elsewhere within one subnormal step
+    normal = np.abs(a) >= 2.0 ** -14
+    assert normal.mean() > 0.99
+    assert np.array_equal(b[normal], a[normal] * 4.0)
+    assert np.all(np.abs(b - a * 4.0) <= 4 * 2.0 ** -24)
+
+
+def test_workspace_poison_and_reuse():
+    import torch
+
+    w = W.build(seed=44, batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                lengths=[3000, 1200])
+    out, t = run(w)
+    ref = to_np(out)
+    plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"],
+                         k_pool=t["k_pool"], max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"])
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=device())
+    for fill in (0xFF, 0x7F, 0x00):  # NaN patterns and zeros
+        ws.fill_(fill)
+        y = to_np(run(w, tensors=t, workspace=ws)[0])
+        assert np.array_equal(y.view(np.uint16), ref.view(np.uint16)), hex(fill)
+
+
+def test_output_guard_bytes_untouched():
+    import torch
+
+    w = W.build(seed=45, batch=2, q=8, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                lengths=[500, 0])
+    t = W.device_tensors(w, device())
+    n = w.batch * w.q * w.num_q_heads * w.head_dim
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), 12345.0, dtype=torch.float16, device=device())
+    out = buf[guard:guard + n].view(w.batch, w.q, w.num_q_heads, w.head_dim)
+    run(w, tensors=t, out=out)
+    host = to_np(buf)
+    assert np.all(host[:guard] == np.float16(12345.0)) and np.all(host[guard + n:] == np.float16(12345.0))
+    judge(host[guard:guard + n].reshape(out.shape), oracle_ref(w), "guarded out")
+
+
+def test_two_streams_two_workspaces():
+    import torch
+
+    w = W.build(seed=46, batch=1, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64, lengths=[4000])
+    t = W.device_tensors(w, device())
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        o1 = run(w, tensors=t, stream=s1)[0]
+    with torch.cuda.stream(s2):
+        o2 = run(w, tensors=t, stream=s2)[0]
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(o1).view(np.uint16), to_np(o2).view(np.uint16))

@@ -301,3 +301,31 @@ def test_golden_stride_counterexample_arithmetic():
     assert s_tok % 8 == 0 and s_tok % 16 != 0
     assert g["second_token_first_byte"] == s_tok
     assert (s_tok // 16) * 16 == g["paired_loader_would_read_from"]
+
+
+def test_midpoint_construction_discriminates():
+    """Negative control (CPU): the midpoint cells tell the pages' two partial
+    representations apart. Normalized per-split outputs rounded to FP16 (the
+    legacy representation "[Bugfix] Use FP32 state and E4M3 defaults for
+    DFlash2" removes) misround at least one tie, while FP32 (max, sum,
+    unnormalized PV) partials combined once round every tie like RNE(exact)."""
+    n, T = 2 ** 16, 1024
+    rng = np.random.default_rng(0)
+    legacy_bad = 0
+    for c in (256, 768, 1280, 1792):
+        for trial in range(8):
+            v = np.ones(n, np.float32)
+            v[rng.choice(n, size=c, replace=False)] = np.float32(1.125)
+            parts = v.reshape(-1, T)
+            exact = (1.0 + c * 2.0 ** -19) * 2.0 ** -6
+            want = np.float16(exact).view(np.uint16)
+            # FP32 unnormalized partials, one final normalization
+            acc = parts.sum(axis=1, dtype=np.float32)
+            l = np.full(len(acc), np.float32(T))
+            y32 = np.float32(acc.sum(dtype=np.float32) * np.float32(2.0 ** -6)) / np.float32(l.sum(dtype=np.float32))
+            assert np.float16(y32).view(np.uint16) == want
+            # normalized split outputs rounded to FP16, then averaged
+            o16 = (acc / np.float32(T)).astype(np.float16).astype(np.float32)
+            y16 = np.float32(o16.mean(dtype=np.float32)) * np.float32(2.0 ** -6)
+            legacy_bad += int(np.float16(y16).view(np.uint16) != want)
+    assert legacy_bad > 0
