@@ -36,6 +36,9 @@ def flags() -> list:
         "-shared",
         "-Wall",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs: the online-softmax rescale is VALU
+        # work on them, and AGPR-resident accumulators would be copied around it
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.dirname(HERE),
     ]
 

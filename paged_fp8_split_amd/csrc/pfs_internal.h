@@ -12,9 +12,9 @@ constexpr int kPartitionTokens = 64;  // the K64 partition: unit of work and of 
 constexpr int kWaves = 4;             // waves per split workgroup
 constexpr int kMaxQHeads = 256;
 constexpr int kMaxQ = 16;
-// Largest (rows x head_dim) one split workgroup holds as FP32 accumulators:
-// 256 accumulator registers per lane x 64 lanes.
-constexpr int kMaxRowsTimesDim = 16384;
+// 16-row MFMA tiles per split workgroup: the FP32 accumulators (rows x head_dim
+// per wave) stay within 128 VGPRs per lane.
+constexpr int max_row_tiles(int head_dim) { return head_dim >= 256 ? 2 : 4; }
 constexpr int kDefaultTargetWorkgroups = 512;
 
 }  // namespace pfs

@@ -5,8 +5,9 @@
 //   pfs_dequant_kernel    paged E4M3 -> dense FP16 bridge
 //   pfs_split_kernel      per-split QK^T (MFMA), online softmax, PV (MFMA);
 //                         emits FP32 (max, sum, unnormalized PV) per split
-//   pfs_combine_kernel    rescales the splits, sums them in ascending split
-//                         order, normalizes and rounds once to FP16
+//   pfs_combine_kernel    rescales the splits, sums them in a fixed order
+//                         (ascending runs, runs in order), normalizes and
+//                         rounds once to FP16
 //
 // The method ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32
 // partials", final status, revision 3 bullet; "[Kernel] Finalize the audited
@@ -18,10 +19,10 @@
 //
 // Work decomposition of the split kernel (one workgroup = 4 waves per split,
 // KV head and row block):
-//  * rows: all R = G*q query rows of one KV head live in one workgroup (row
-//    r = i*G + jj: draft row i, jj-th query head of the group), padded to 16-row
-//    MFMA tiles; the FP32 accumulators of every row and every head_dim column
-//    stay in registers (R*D <= 16384 -> <= 256 accumulators per lane).
+//  * rows: up to 64 of the R = G*q query rows of one KV head per workgroup
+//    (row r = i*G + jj: draft row i, jj-th query head of the group), padded to
+//    16-row MFMA tiles; more rows become row blocks of the grid. The FP32
+//    accumulators of every row and every head_dim column stay in registers.
 //  * tokens: wave w takes partitions w, w+4, w+8, ... of the split, in
 //    ascending order; the four wave states are merged in wave order at the end.
 //  * scores are computed transposed, S^T = K * Q^T (A = K: 16 tokens x 32 dims,
@@ -31,21 +32,21 @@
 //  * K goes from HBM straight into MFMA A operands: lane (c, g) of a 16-token
 //    tile loads 16-byte chunks of token c, so each load instruction reads 64
 //    contiguous bytes of 16 tokens; the E4M3 bytes are converted in registers.
-//  * V^T needs 8 tokens of one head_dim column per lane: lane (c, g) loads
-//    head_dim/16 contiguous bytes (a column strip) of each of its 8 tokens,
-//    then v_perm_b32 interleaves the bytes of token pairs so every
-//    v_cvt_scalef32_pk_f16_fp8 yields two tokens of one column. Each load
-//    instruction reads 4 whole token rows.
+//  * V^T needs 8 tokens of one head_dim column per lane: V rows are loaded
+//    with 16-byte loads (4 whole token rows per instruction), written to the
+//    wave's LDS stage with an XOR swizzle of the 16-byte chunks, and read back
+//    transposed with ds_read_b64_tr_b8: in each 16-lane block, lane j names
+//    8 bytes of one token row and every lane receives one column of 8 tokens.
 //  * Q^T operands are staged once per workgroup in LDS in the exact per-lane
 //    order the MFMA B operand needs (one ds_read_b128 per operand).
 //
 // Numerics: FP16 MFMA operands with FP32 accumulation; the per-head K scale,
 // the softmax scale and log2(e) are applied to FP32 scores; probabilities are
-// exp2(s - m + 15) rounded once to FP16 (the 2^15 offset keeps them out of the
-// FP16 subnormal range and cancels in acc / l); the running sum accumulates the
-// same rounded values the PV product uses; V's scale is applied once in the
-// combine. Masked scores are selected to -inf and K/V bytes beyond the live
-// length are never loaded (zero), so NaN tail bytes cannot leak.
+// exp2(s - m_ref + 7) rounded once to FP16 against a lazily raised reference
+// maximum m_ref; the row sums come from the matrix core (a ones row times the
+// same FP16 P the PV product uses); V's scale is applied once in the combine.
+// Masked scores are selected to -inf and K/V bytes beyond the live length are
+// never loaded (zero), so NaN tail bytes cannot leak.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -59,12 +60,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = pfs::kWaves;
 constexpr int kPart = pfs::kPartitionTokens;
 constexpr int kStep = 32;  // tokens per MFMA fold step (two 16-token tiles)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kPBias = 15.0f;  // P = exp2(s - m + 15) <= 32768
 
 template <typename T, typename F>
 __device__ __forceinline__ T bit_cast_(F f) {
@@ -96,12 +97,6 @@ __device__ __forceinline__ float wave_max_xor_16_32(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
 __device__ __forceinline__ int32_t clamp_i(int64_t v, int64_t lo, int64_t hi) {
     return (int32_t)(v < lo ? lo : (v > hi ? hi : v));
 }
@@ -128,69 +123,62 @@ struct SplitArgs {
     int32_t max_pages;
     int32_t capacity;
     int32_t tokens_per_split;
+    int32_t num_splits;
     int32_t row_blocks;
     float sm_scale_log2e;
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-template <int D>
-struct VChunk;  // the head_dim/16 bytes of one token a lane loads for V
-template <>
-struct VChunk<64> {
-    static constexpr int kDwords = 1;
-    typedef uint32_t type;
-};
-template <>
-struct VChunk<128> {
-    static constexpr int kDwords = 2;
-    typedef u32x2 type;
-};
-template <>
-struct VChunk<256> {
-    static constexpr int kDwords = 4;
-    typedef u32x4 type;
-};
-
-template <int D>
-__device__ __forceinline__ uint32_t vdword(const typename VChunk<D>::type& v, int i) {
-    if constexpr (D == 64) {
-        return v;
-    } else {
-        return v[i];
-    }
-}
-
-// Per-wave state of the split kernel.
+// Compile-time geometry of the split kernel.
 template <int D, int RT>
-struct WaveState {
-    static constexpr int MD = D / 16;  // PV output tiles along head_dim
-    f32x4 acc[MD][RT];                 // O^T tiles: [d tile][row tile]
-    float m[RT];                       // running max (log2 domain) of this lane's row in each row tile
-    float l[RT];                       // running sum, partial over this lane's token slots
+struct SplitCfg {
+    static constexpr int KSTEPS = D / 32;             // QK k-steps (32 dims each)
+    static constexpr int CH = D / 16;                 // 16-byte chunks per token row
+    static constexpr int LOADS = CH / 2;              // 16-byte loads per lane per 32-token step (K or V)
+    static constexpr int MD = D / 16;                 // PV tiles along head_dim
+    static constexpr int QBYTES = RT * KSTEPS * 64 * 16;
+    static constexpr int STAGE = kStep * D;           // one wave's K (or V) stage: 32 token rows
+    static constexpr int MERGE_BYTES = MD * RT * 64 * 16;
+    static constexpr int MAIN_BYTES = QBYTES + kWaves * 2 * STAGE;
+    static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
 };
+
+// Lazy rescaling: a row's exponentials use a reference maximum m_ref and are
+// exp2(s*c - m_ref + kPBias). m_ref is raised (and the accumulators rescaled)
+// only when a score exceeds it by more than kTau, so P <= 2^(kPBias + kTau) =
+// 2^15 stays an FP16 number, and P only becomes FP16-subnormal for terms below
+// 2^-21 of the reference maximum. The offset cancels in acc / l.
+constexpr float kTau = 8.0f;
+constexpr float kPBias = 7.0f;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every tile: the load returns zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 template <int D, int RT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 pfs_split_kernel(const SplitArgs a) {
-    constexpr int KSTEPS = D / 32;  // QK k-steps (32 dims each)
-    constexpr int KLOADS = D / 64;  // 16-byte K loads per lane per 16-token tile
-    constexpr int MD = D / 16;      // PV tiles along head_dim
-    constexpr int VD = VChunk<D>::kDwords;
-    constexpr int kQSlots = RT * KSTEPS * 64;          // 16-byte Q operand slots
-    constexpr int kMergeSlots = MD * RT * 64;          // 16-byte accumulator slots of one wave
-    constexpr int kLdsSlots = kQSlots > kMergeSlots ? kQSlots : kMergeSlots;
-    __shared__ u32x4 lds[kLdsSlots];
+    using C = SplitCfg<D, RT>;
+    constexpr int KSTEPS = C::KSTEPS, CH = C::CH, LOADS = C::LOADS, MD = C::MD;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
     __shared__ float2 lds_ml[kWaves][RT * 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lc = lane & 15;   // column within a 16-wide MFMA tile
-    const int lg = lane >> 4;   // lane group (k-group / row-quad)
+    const int lc = lane & 15;  // column within a 16-wide MFMA tile
+    const int lg = lane >> 4;  // lane group (k-group of an operand, row-quad of a result)
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y / a.row_blocks;
-    const int rb = blockIdx.y % a.row_blocks;
-    const int b = blockIdx.z;
+    // 1-D grid. Workgroups x and x + 8 run on the same XCD (dispatch is
+    // round-robin over the 8 XCDs), so the row blocks of one (split, KV head,
+    // request) get ids 8 apart and share that XCD's L2 for their K/V reads.
+    const int x = blockIdx.x;
+    const int rb = (x >> 3) % a.row_blocks;
+    const int unit = ((x >> 3) / a.row_blocks) * 8 + (x & 7);  // (split, KV head, request), split fastest
+    if (unit >= a.num_splits * a.num_kv_heads * a.batch) return;
+    const int split = unit % a.num_splits;
+    const int g = (unit / a.num_splits) % a.num_kv_heads;
+    const int b = unit / (a.num_splits * a.num_kv_heads);
 
     const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
     const int32_t tok0 = split * a.tokens_per_split;
@@ -198,8 +186,13 @@ pfs_split_kernel(const SplitArgs a) {
     const int32_t tok1 = min(tok0 + a.tokens_per_split, L);
     const int r_begin = rb * RT * 16;
 
-    // ---- stage Q^T operands in LDS (slot = (nt * KSTEPS + ks) * 64 + lane) ----
-    for (int slot = threadIdx.x; slot < kQSlots; slot += 256) {
+    u32x4* q_lds = reinterpret_cast<u32x4*>(smem);
+    uint8_t* k_lds = smem + C::QBYTES + wave * 2 * C::STAGE;
+    uint8_t* v_lds = k_lds + C::STAGE;
+
+    // ---- stage Q^T operands in LDS: slot (nt * KSTEPS + ks) * 64 + lane holds
+    //      row r_begin + 16 nt + (lane & 15), dims 64(ks/2) + 16(lane/16) + 8(ks&1) + [0, 8) ----
+    for (int slot = threadIdx.x; slot < RT * KSTEPS * 64; slot += 256) {
         const int ln = slot & 63;
         const int ks = (slot >> 6) % KSTEPS;
         const int nt = (slot >> 6) / KSTEPS;
@@ -209,177 +202,204 @@ pfs_split_kernel(const SplitArgs a) {
         if (r < a.rows) {
             const int i = r / a.group;
             const int h = a.qhead[g * a.group + (r % a.group)];
-            const _Float16* src = a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + d0;
-            v = *reinterpret_cast<const u32x4*>(src);
+            v = *reinterpret_cast<const u32x4*>(a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + d0);
         }
-        lds[slot] = v;
+        q_lds[slot] = v;
     }
 
-    // causal limit of this lane's row in each row tile: keys [0, lim) are visible
+    // causal limit of this lane's row in each row tile: keys [0, lim) are visible.
+    // Padding rows (r >= rows) keep lim = L: their Q is zero, their results are
+    // never written and MFMA columns do not mix, so they need no masking.
     int32_t lim[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
         const int r = r_begin + nt * 16 + lc;
-        lim[nt] = (r < a.rows) ? clamp_i((int64_t)L - a.q + r / a.group + 1, 0, L) : 0;
+        lim[nt] = (r < a.rows) ? clamp_i((int64_t)L - a.q + r / a.group + 1, 0, L) : L;
     }
+    const int32_t lim_lo = clamp_i((int64_t)L - a.q + 1, 0, L);  // smallest limit of any real row
     const float cscale = a.sm_scale_log2e * a.kscale[g];
 
-    WaveState<D, RT> st;
+    f32x4 acc[MD][RT];
+    f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
+    float mref[RT], nb[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
-        st.m[nt] = -INFINITY;
-        st.l[nt] = 0.0f;
+        mref[nt] = -INFINITY;
+        nb[nt] = 0.0f;
+        lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int md = 0; md < MD; ++md) st.acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int md = 0; md < MD; ++md) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // A operand of the row-sum tile: row 0 all ones, rows 1..15 zero
+    const _Float16 one_or_zero = (lc == 0) ? (_Float16)1.0f : (_Float16)0.0f;
+    const f16x8 ones = f16x8{one_or_zero, one_or_zero, one_or_zero, one_or_zero,
+                             one_or_zero, one_or_zero, one_or_zero, one_or_zero};
+
+    // Load slot j of a lane: 16-byte chunk c = lane % CH of token row
+    // t_j = (64 j + lane) / CH of the 32-token step (each instruction reads
+    // 64 / CH whole rows). In LDS, row t keeps its chunks XOR-swizzled by t % CH.
+    const int ld_c = lane % CH;
+    const uint32_t ld_voff_base = 16u * (uint32_t)ld_c;
+    // transposed V reads: lane j of each 16-lane block names 8 bytes of token
+    // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk
+    const int tr_tok = ((lc >> 1) < 4 ? 0 : 16) + 4 * lg + ((lc >> 1) & 3);
+    const int tr_base = tr_tok * D + 8 * (lc & 1);
+    const int tr_sw = tr_tok % CH;
+
     __syncthreads();
 
     const int64_t head_off = (int64_t)g * a.head_stride;
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+    const uint32_t tile_bytes = (uint32_t)(15 * a.token_stride + D);
     const int32_t p_begin = tok0 / kPart;
     const int32_t p_end = (tok1 + kPart - 1) / kPart;
+    // this wave's steps: partitions p_begin + wave + 4k, two 32-token steps each
+    const int32_t nparts = (p_end - p_begin - wave + kWaves - 1) / kWaves;
+    int32_t nsteps = 0;
+    if (nparts > 0) {
+        const int32_t last_part = p_begin + wave + (nparts - 1) * kWaves;
+        nsteps = 2 * nparts - ((last_part * kPart + kStep) >= L ? 1 : 0);
+    }
+    auto step_token = [&](int32_t st) -> int32_t {
+        return (p_begin + wave + (st >> 1) * kWaves) * kPart + (st & 1) * kStep;
+    };
 
-    for (int32_t part = p_begin + wave; part < p_end; part += kWaves) {
-#pragma unroll 1
-        for (int half = 0; half < 2; ++half) {
-            const int32_t t_step = part * kPart + half * kStep;
-            if (t_step >= L) break;
-            // pages of the two 16-token tiles (page_size is a multiple of 16)
-            const bool live1 = t_step + 16 < L;
-            const int64_t pg0 = (int64_t)bt_row[t_step / a.page_size] * a.page_stride +
-                                (int64_t)(t_step % a.page_size) * a.token_stride + head_off;
-            const int64_t pg1 = live1 ? (int64_t)bt_row[(t_step + 16) / a.page_size] * a.page_stride +
-                                            (int64_t)((t_step + 16) % a.page_size) * a.token_stride + head_off
-                                      : 0;
-
-            // ---- V loads: 8 tokens x head_dim/16 bytes (column strip lc) ----
-            typename VChunk<D>::type vraw[8];
+    // ---- loads of one 32-token step into registers (tokens >= L read as zeros) ----
+    u32x4 kreg[LOADS], vreg[LOADS];
+    auto load_step = [&](int32_t t_step) {
+        const bool live1 = t_step + 16 < L;
+        const int64_t off0 = (int64_t)bt_row[t_step / a.page_size] * a.page_stride +
+                             (int64_t)(t_step % a.page_size) * a.token_stride + head_off;
+        const int64_t off1 = live1 ? (int64_t)bt_row[(t_step + 16) / a.page_size] * a.page_stride +
+                                         (int64_t)((t_step + 16) % a.page_size) * a.token_stride + head_off
+                                   : 0;
+        const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(a.kpool + off0, tile_bytes);
+        const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(a.kpool + off1, tile_bytes);
+        const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(a.vpool + off0, tile_bytes);
+        const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(a.vpool + off1, tile_bytes);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tt = (e < 4 ? 0 : 16) + 4 * lg + (e & 3);  // token within the step
-                const bool ok = t_step + tt < L;
-                const int64_t off = (e < 4 ? pg0 : pg1) + (int64_t)(tt & 15) * a.token_stride + lc * (D / 16);
-                if (ok) {
-                    vraw[e] = *reinterpret_cast<const typename VChunk<D>::type*>(a.vpool + off);
-                } else {
-                    vraw[e] = typename VChunk<D>::type{};
-                }
-            }
+        for (int j = 0; j < LOADS; ++j) {
+            const int t = (64 * j + lane) / CH;  // token of the step; the 16-token tile is uniform in j
+            const uint32_t voff = (t_step + t < L) ? (uint32_t)(t & 15) * (uint32_t)a.token_stride + ld_voff_base
+                                                   : kOutOfRange;
+            const bool tile1 = (64 * j) / CH >= 16;
+            kreg[j] = bit_cast_<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(tile1 ? k1 : k0, voff, 0, 0));
+            vreg[j] = bit_cast_<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(tile1 ? v1 : v0, voff, 0, 0));
+        }
+    };
 
-            // ---- K loads: 2 tiles x KLOADS x 16 bytes ----
-            u32x4 kraw[2][KLOADS];
+    if (nsteps > 0) load_step(step_token(0));
+
+    for (int32_t st = 0; st < nsteps; ++st) {
+        const int32_t t_step = step_token(st);
+        // this step's K and V -> the wave's LDS stages, then prefetch the next step
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int t = (64 * j + lane) / CH;
+            const int off = t * D + ((ld_c ^ (t % CH)) << 4);
+            *reinterpret_cast<u32x4*>(k_lds + off) = kreg[j];
+            *reinterpret_cast<u32x4*>(v_lds + off) = vreg[j];
+        }
+        if (st + 1 < nsteps) load_step(step_token(st + 1));
+
+        // ---- S^T = K * Q^T ----
+        f32x4 s[2][RT];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            f16x8 qop[RT];
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) qop[nt] = bit_cast_<f16x8>(q_lds[(nt * KSTEPS + ks) * 64 + lane]);
+            const int chunk = 4 * (ks >> 1) + lg;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const bool ok = t_step + mt * 16 + lc < L;
-                const int64_t off = (mt == 0 ? pg0 : pg1) + (int64_t)lc * a.token_stride + 16 * lg;
+                const int t = 16 * mt + lc;
+                const u32x2 w = *reinterpret_cast<const u32x2*>(k_lds + t * D + ((chunk ^ (t % CH)) << 4) +
+                                                                8 * (ks & 1));
+                const f16x8 kop = e4m3x8_to_f16x8(w.x, w.y);
 #pragma unroll
-                for (int j = 0; j < KLOADS; ++j) {
-                    if (ok) {
-                        kraw[mt][j] = *reinterpret_cast<const u32x4*>(a.kpool + off + 64 * j);
-                    } else {
-                        kraw[mt][j] = u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
+                for (int nt = 0; nt < RT; ++nt)
+                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[nt], s[mt][nt], 0, 0, 0);
             }
+        }
 
-            // ---- S^T = K * Q^T ----
-            f32x4 s[2][RT];
+        // ---- online softmax, log2 domain, lazy reference maximum ----
+        const bool edge = t_step + kStep > lim_lo;  // some (row, token) of this step is masked
+        float smax[RT];
+        bool need = false;
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) {
+            float mx = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < RT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                f16x8 qop[RT];
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt) qop[nt] = bit_cast_<f16x8>(lds[(nt * KSTEPS + ks) * 64 + lane]);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const u32x4 w = kraw[mt][ks >> 1];
-                    const f16x8 kop = (ks & 1) ? e4m3x8_to_f16x8(w.z, w.w) : e4m3x8_to_f16x8(w.x, w.y);
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt)
-                        s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[nt], s[mt][nt], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    float v = s[mt][nt][i];
+                    if (edge) {
+                        const int32_t t = t_step + mt * 16 + 4 * lg + i;
+                        v = (t < lim[nt]) ? v : -INFINITY;
+                        s[mt][nt][i] = v;
+                    }
+                    mx = fmaxf(mx, v);
                 }
-            }
-
-            // ---- online softmax (log2 domain) ----
-            f16x8 pop[RT];
-            float alpha[RT];
-            bool rescale = false;
+            mx = wave_max_xor_16_32(mx);
+            smax[nt] = mx * cscale;  // cscale > 0; -inf stays -inf
+            need |= (smax[nt] > mref[nt] + kTau);
+        }
+        if (__any(need)) {
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) {
-                float x[8];
+                const float m_new = fmaxf(mref[nt], smax[nt]);
+                if (m_new != mref[nt]) {
+                    const float al = (mref[nt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mref[nt] - m_new);
+                    lacc[nt] *= al;
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int32_t t = t_step + mt * 16 + 4 * lg + i;
-                        x[mt * 4 + i] = (t < lim[nt]) ? s[mt][nt][i] * cscale : -INFINITY;
-                    }
-                float mx = x[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-                mx = wave_max_xor_16_32(mx);
-                const float m_new = fmaxf(st.m[nt], mx);
-                float al = 1.0f;
-                if (m_new != -INFINITY && st.m[nt] != m_new) al = __builtin_amdgcn_exp2f(st.m[nt] - m_new);
-                rescale |= (al != 1.0f);
-                alpha[nt] = al;
-                float lsum = 0.0f;
-                _Float16 ph[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x[e] - m_new) + kPBias);
-                    ph[e] = (_Float16)pv;
-                    lsum += (float)ph[e];
-                }
-                st.l[nt] = st.l[nt] * al + lsum;
-                st.m[nt] = m_new;
-                pop[nt] = f16x8{ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
-            }
-            if (__any(rescale)) {
-#pragma unroll
-                for (int md = 0; md < MD; ++md)
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt) st.acc[md][nt] *= alpha[nt];
-            }
-
-            // ---- O^T += V^T * P^T ----
-#pragma unroll
-            for (int q4 = 0; q4 < VD; ++q4) {
-                u32x4 op[4];  // V^T operands for d tiles 4*q4 .. 4*q4+3
-#pragma unroll
-                for (int pr = 0; pr < 4; ++pr) {
-                    const uint32_t w0 = vdword<D>(vraw[2 * pr], q4);
-                    const uint32_t w1 = vdword<D>(vraw[2 * pr + 1], q4);
-                    const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // b0 of w0,w1 | b1 of w0,w1
-                    const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // b2 of w0,w1 | b3 of w0,w1
-                    op[0][pr] = e4m3x2_to_f16x2<false>(lo);
-                    op[1][pr] = e4m3x2_to_f16x2<true>(lo);
-                    op[2][pr] = e4m3x2_to_f16x2<false>(hi);
-                    op[3][pr] = e4m3x2_to_f16x2<true>(hi);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const f16x8 vop = bit_cast_<f16x8>(op[u]);
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt)
-                        st.acc[4 * q4 + u][nt] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], st.acc[4 * q4 + u][nt], 0, 0, 0);
+                    for (int md = 0; md < MD; ++md) acc[md][nt] *= al;
+                    mref[nt] = m_new;
+                    nb[nt] = kPBias - m_new;
                 }
             }
         }
+        f16x8 pop[RT];
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) {
+            _Float16 ph[8];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = s[mt][nt][i];
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(v, cscale, nb[nt]));
+                    ph[mt * 4 + i] = (_Float16)((edge && v == -INFINITY) ? 0.0f : pv);
+                }
+            pop[nt] = f16x8{ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
+        }
+
+        // ---- O^T += V^T * P^T (V^T read transposed from LDS), l += 1 * P^T ----
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+            const int addr = tr_base + ((md ^ tr_sw) << 4);
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(v_lds + addr));
+            const f16x8 vop = e4m3x8_to_f16x8((uint32_t)w.x, (uint32_t)w.y);
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt)
+                acc[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
     }
 
     // ---- merge the four wave states in wave order ----
-#pragma unroll
-    for (int nt = 0; nt < RT; ++nt) st.l[nt] = wave_sum_xor_16_32(st.l[nt]);
+    // row sums live in result row 0 of the ones tile: lanes of lane group 0, element 0
     if (lg == 0) {
 #pragma unroll
-        for (int nt = 0; nt < RT; ++nt) lds_ml[wave][nt * 16 + lc] = make_float2(st.m[nt], st.l[nt]);
+        for (int nt = 0; nt < RT; ++nt) lds_ml[wave][nt * 16 + lc] = make_float2(mref[nt], lacc[nt][0]);
     }
-    __syncthreads();  // also: every wave is done reading Q from lds
+    __syncthreads();  // every wave is also done with Q, K and V in LDS from here on
     float M[RT], Ltot[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
@@ -397,46 +417,38 @@ pfs_split_kernel(const SplitArgs a) {
         M[nt] = mm;
         Ltot[nt] = lt;
 #pragma unroll
-        for (int md = 0; md < MD; ++md) st.acc[md][nt] *= fmine;
+        for (int md = 0; md < MD; ++md) acc[md][nt] *= fmine;
     }
+    u32x4* mbuf = reinterpret_cast<u32x4*>(smem);
     for (int w = 1; w < kWaves; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int nt = 0; nt < RT; ++nt) lds[(md * RT + nt) * 64 + lane] = bit_cast_<u32x4>(st.acc[md][nt]);
+                for (int nt = 0; nt < RT; ++nt) mbuf[(md * RT + nt) * 64 + lane] = bit_cast_<u32x4>(acc[md][nt]);
         }
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
             for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int nt = 0; nt < RT; ++nt)
-                    st.acc[md][nt] += bit_cast_<f32x4>(lds[(md * RT + nt) * 64 + lane]);
+                for (int nt = 0; nt < RT; ++nt) acc[md][nt] += bit_cast_<f32x4>(mbuf[(md * RT + nt) * 64 + lane]);
         }
         __syncthreads();
     }
     if (wave != 0) return;
 
-    // ---- emit the split partial: (max, sum) and the unnormalized PV ----
+    // ---- emit the split partial: (reference max, sum) and the unnormalized PV ----
+    // accumulator element i of d tile md is column 16 md + 4 lg + i of row r
     const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
         const int r = r_begin + nt * 16 + lc;
         if (r >= a.rows) continue;
         if (lg == 0) reinterpret_cast<float2*>(a.ws_ml)[slot_base + r] = make_float2(M[nt], Ltot[nt]);
-        float* dst = a.ws_acc + (slot_base + r) * D;
+        float* dst = a.ws_acc + (slot_base + r) * D + 4 * lg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // accumulator element i of every d tile md is column (4*lg + i) * MD + md
-            float vals[MD];
-#pragma unroll
-            for (int md = 0; md < MD; ++md) vals[md] = st.acc[md][nt][i];
-            float* p = dst + (4 * lg + i) * MD;
-#pragma unroll
-            for (int k = 0; k < MD; k += 4)
-                *reinterpret_cast<f32x4*>(p + k) = f32x4{vals[k], vals[k + 1], vals[k + 2], vals[k + 3]};
-        }
+        for (int md = 0; md < MD; ++md) *reinterpret_cast<f32x4*>(dst + 16 * md) = acc[md][nt];
     }
 }
 
@@ -457,15 +469,19 @@ struct CombineArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// One workgroup (4 waves) per output row (request, KV head, row). Wave w sums
-// a contiguous quarter of the visible splits in ascending order; the quarters
-// are then added in wave order. Each lane owns head_dim/64 columns.
+// One workgroup of 16 waves per output row (request, KV head, row). Wave w
+// sums the w-th contiguous run of the visible splits in ascending split order
+// (its loads are independent, so a wave keeps its whole run in flight); the 16
+// runs are then added in wave order. The global max is a plain max (exact, so
+// any order). Each lane owns head_dim/64 columns.
+constexpr int kCombineWaves = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const CombineArgs a) {
     constexpr int CPL = D / 64;  // columns per lane
-    __shared__ float red[kWaves];
-    __shared__ float part_l[kWaves];
-    __shared__ float part_acc[kWaves][D];
+    __shared__ float red[kCombineWaves];
+    __shared__ float part_l[kCombineWaves];
+    __shared__ float part_acc[kCombineWaves][D];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -490,16 +506,16 @@ __global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
     const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
 
-    // global max over the visible splits (max is exact: any order)
     float mx = -INFINITY;
-    for (int s = threadIdx.x; s < ns; s += 256) mx = fmaxf(mx, ml[slot0 + s * stride].x);
+    for (int s = threadIdx.x; s < ns; s += 64 * kCombineWaves) mx = fmaxf(mx, ml[slot0 + s * stride].x);
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red[w]);
 
-    // this wave's contiguous quarter of the splits, ascending
-    const int per = (ns + kWaves - 1) / kWaves;
+    const int per = (ns + kCombineWaves - 1) / kCombineWaves;
     const int s0 = wave * per;
     const int s1 = min(ns, s0 + per);
     float lw = 0.0f;
@@ -513,14 +529,15 @@ __global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
         lw += f * v.y;
         const float* src = a.ws_acc + slot * D + lane * CPL;
         if constexpr (CPL == 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(src);
-            acc[0] += f * x[0];
-            acc[1] += f * x[1];
-            acc[2] += f * x[2];
-            acc[3] += f * x[3];
-        } else {
+            const f32x4 xx = *reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[c] += f * src[c];
+            for (int c = 0; c < 4; ++c) acc[c] += f * xx[c];
+        } else if constexpr (CPL == 2) {
+            const float2 xx = *reinterpret_cast<const float2*>(src);
+            acc[0] += f * xx.x;
+            acc[1] += f * xx.y;
+        } else {
+            acc[0] += f * src[0];
         }
     }
     if (lane == 0) part_l[wave] = lw;
@@ -528,12 +545,16 @@ __global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
     for (int c = 0; c < CPL; ++c) part_acc[wave][lane * CPL + c] = acc[c];
     __syncthreads();
     if (wave != 0) return;
-    const float lt = ((part_l[0] + part_l[1]) + part_l[2]) + part_l[3];
+    float lt = part_l[0];
+#pragma unroll
+    for (int w = 1; w < kCombineWaves; ++w) lt += part_l[w];
     const float vs = a.vscale[g];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int d = lane * CPL + c;
-        const float num = ((part_acc[0][d] + part_acc[1][d]) + part_acc[2][d]) + part_acc[3][d];
+        float num = part_acc[0][d];
+#pragma unroll
+        for (int w = 1; w < kCombineWaves; ++w) num += part_acc[w][d];
         dst[d] = (_Float16)((num * vs) / lt);
     }
 }
@@ -568,27 +589,23 @@ __global__ __launch_bounds__(256) void pfs_dequant_kernel(const uint8_t* pool, c
 }
 
 template <int D, int RT>
-hipError_t launch_split(const SplitArgs& a, int32_t num_splits, hipStream_t stream) {
-    const dim3 grid(num_splits, a.num_kv_heads * a.row_blocks, a.batch);
-    hipLaunchKernelGGL((pfs_split_kernel<D, RT>), grid, dim3(256), 0, stream, a);
+hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
+    const int64_t wgs = ((units + 7) / 8) * 8 * a.row_blocks;
+    hipLaunchKernelGGL((pfs_split_kernel<D, RT>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t num_splits, hipStream_t stream) {
+hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, hipStream_t stream) {
     switch (row_tiles) {
-        case 1: return launch_split<D, 1>(a, num_splits, stream);
-        case 2: return launch_split<D, 2>(a, num_splits, stream);
-        case 4: return launch_split<D, 4>(a, num_splits, stream);
-        default: break;
+        case 1: return launch_split<D, 1>(a, stream);
+        case 2: return launch_split<D, 2>(a, stream);
+        case 4:
+            if constexpr (pfs::max_row_tiles(D) >= 4) return launch_split<D, 4>(a, stream);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
     }
-    if constexpr (D <= 128) {
-        if (row_tiles == 8) return launch_split<D, 8>(a, num_splits, stream);
-    }
-    if constexpr (D == 64) {
-        if (row_tiles == 16) return launch_split<D, 16>(a, num_splits, stream);
-    }
-    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -619,6 +636,7 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     sa.max_pages = p.max_pages_per_row;
     sa.capacity = plan->capacity;
     sa.tokens_per_split = plan->tokens_per_split;
+    sa.num_splits = plan->num_splits;
     sa.row_blocks = plan->row_blocks;
     sa.sm_scale_log2e = p.sm_scale * kLog2e;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) sa.qhead[i] = plan->qhead[i];
@@ -626,9 +644,9 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     switch (p.head_dim) {
-        case 64: e = launch_split_d<64>(sa, plan->row_tiles, plan->num_splits, s); break;
-        case 128: e = launch_split_d<128>(sa, plan->row_tiles, plan->num_splits, s); break;
-        case 256: e = launch_split_d<256>(sa, plan->row_tiles, plan->num_splits, s); break;
+        case 64: e = launch_split_d<64>(sa, plan->row_tiles, s); break;
+        case 128: e = launch_split_d<128>(sa, plan->row_tiles, s); break;
+        case 256: e = launch_split_d<256>(sa, plan->row_tiles, s); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
@@ -655,9 +673,9 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid(plan->rows, p.num_kv_heads, p.batch);
     switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, dim3(256), 0, s, ca); break;
-        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, dim3(256), 0, s, ca); break;
-        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, dim3(256), 0, s, ca); break;
+        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
+        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
+        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;

@@ -19,8 +19,8 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // that holds all rows, capped by the accumulator budget; the rest becomes row
 // blocks along the grid.
 void choose_row_tiles(int32_t rows, int32_t head_dim, int32_t* tiles, int32_t* blocks) {
-    const int32_t max_tiles = pfs::kMaxRowsTimesDim / (16 * head_dim);  // 4, 8 or 16
-    static const int32_t kTiles[] = {1, 2, 4, 8, 16};
+    const int32_t max_tiles = pfs::max_row_tiles(head_dim);
+    static const int32_t kTiles[] = {1, 2, 4};
     int32_t need = (rows + 15) / 16;
     if (need > max_tiles) {
         *tiles = max_tiles;
