@@ -8,10 +8,12 @@ E4M3 K/V with per-head scales and 1% outlier tokens, page size 64 (the
 resident in HBM before the timed region starts.
 
 Timing: W untimed warmup steps, then K timed steps. Before every timed step an
-untimed 1 GiB write evicts the 256 MB Infinity Cache, so the KV bytes come
-from HBM; each step is bracketed by HIP events recorded on the stream the
-kernels run on (split: e0 -> e1, combine: e1 -> e2). The whole timed loop is
-also bracketed by a device synchronize.
+untimed read of a clean 1 GiB buffer evicts the 256 MB Infinity Cache and the
+L2s, so the KV bytes come from HBM. The scrub only reads: a scrub that writes
+leaves dirty lines whose write-back then competes with the timed kernel's
+reads. Each step is bracketed by HIP events recorded on the stream the kernels
+run on (split: e0 -> e1, combine: e1 -> e2). The whole timed loop is also
+bracketed by a device synchronize.
 
 Prints one JSON line. `value` is the achieved KV read rate: live K+V bytes of
 the step divided by the mean step time.
@@ -111,6 +113,8 @@ def main() -> int:
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (to scale HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,6 +125,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return 0
 
     import paged_fp8_split_amd as pfs
     from paged_fp8_split_amd import _lib
@@ -135,7 +149,13 @@ def main() -> int:
                          tokens_per_split=args.tokens_per_split)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["q"])
-    scrub = None if args.no_scrub else torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    scrub = None if args.no_scrub else torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read only
+    scrub_sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, 0, out=scrub_sink)
     stream = torch.cuda.current_stream(dev)
 
     def split():
@@ -147,8 +167,7 @@ def main() -> int:
 
     note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B")
     for _ in range(args.warmup):
-        if scrub is not None:
-            scrub.add_(1.0)
+        evict()
         split()
         combine()
     torch.cuda.synchronize()
@@ -158,8 +177,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for k in range(args.steps):
-        if scrub is not None:
-            scrub.add_(1.0)
+        evict()
         evs[k][0].record(stream)
         split()
         evs[k][1].record(stream)

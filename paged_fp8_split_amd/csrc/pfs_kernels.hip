@@ -51,6 +51,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "pfs_internal.h"
 
 namespace {
@@ -62,8 +65,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = pfs::kWaves;
-constexpr int kPart = pfs::kPartitionTokens;
 constexpr int kStep = 32;  // tokens per MFMA fold step (two 16-token tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -91,10 +92,14 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
     return bit_cast_<f16x8>(r);
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+// Max over the four lanes l, l^16, l^32, l^48 (the lane groups holding one
+// result column). v_permlane16/32_swap return both halves of a swap; the max
+// of the pair is the xor-16 / xor-32 butterfly step, identical in every lane.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 __device__ __forceinline__ int32_t clamp_i(int64_t v, int64_t lo, int64_t hi) {
@@ -120,6 +125,7 @@ struct SplitArgs {
     int32_t group;
     int32_t rows;
     int32_t page_size;
+    int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
     int32_t max_pages;
     int32_t capacity;
     int32_t tokens_per_split;
@@ -129,18 +135,31 @@ struct SplitArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// Compile-time geometry of the split kernel.
-template <int D, int RT>
+// Compile-time geometry of the split kernel: RT 16-row tiles per wave, RG row
+// groups x TP token lanes = 4 waves, NS LDS stages of TP 32-token steps.
+template <int D, int RT, int RG, int TP, int NS>
 struct SplitCfg {
-    static constexpr int KSTEPS = D / 32;             // QK k-steps (32 dims each)
-    static constexpr int CH = D / 16;                 // 16-byte chunks per token row
-    static constexpr int LOADS = CH / 2;              // 16-byte loads per lane per 32-token step (K or V)
-    static constexpr int MD = D / 16;                 // PV tiles along head_dim
-    static constexpr int QBYTES = RT * KSTEPS * 64 * 16;
-    static constexpr int STAGE = kStep * D;           // one wave's K (or V) stage: 32 token rows
-    static constexpr int MERGE_BYTES = MD * RT * 64 * 16;
-    static constexpr int MAIN_BYTES = QBYTES + kWaves * 2 * STAGE;
-    static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+    static constexpr int W = RG * TP;
+    static_assert(W == pfs::kWaves, "four waves per split workgroup");
+    static constexpr int KSTEPS = D / 32;           // QK k-steps (32 dims each)
+    static constexpr int KLOADS = D / 64;           // 1 KB loads per 16-token K tile
+    static constexpr int CH = D / 16;               // 16-byte chunks per token row
+    static constexpr int MD = D / 16;               // PV tiles along head_dim
+    static constexpr int STEP_LOADS = D / 16;       // 1 KB loads per 32-token step: K tile 0, K tile 1, V
+    static constexpr int STEP_BYTES = 1024 * STEP_LOADS;
+    static constexpr int V_OFF = 1024 * (D / 32);   // V rows within a step
+    static constexpr int STAGE_BYTES = TP * STEP_BYTES;
+    static constexpr int NW = STEP_LOADS / RG;      // loads per wave per stage
+    static constexpr int ACC_SLOTS = MD * RT * 64;  // 16-byte slots of one wave's accumulators
+    // md tiles merged per round so that one tree level of writers fits in stage 0
+    static constexpr int MERGE_MD = TP > 1 ? (STAGE_BYTES / (RG * (TP / 2) * RT * 1024) < MD
+                                                  ? STAGE_BYTES / (RG * (TP / 2) * RT * 1024)
+                                                  : MD)
+                                           : MD;
+    static_assert(TP == 1 || (MERGE_MD >= 1 && MD % MERGE_MD == 0), "merge chunking");
+    static_assert(NS == 2 || NS == 4 || NS == 8, "stages");
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES + 8 * pfs::kPageTableEntries;
+    static constexpr int WAVES_PER_EU = pfs::split_workgroups_per_cu(D, TP, NS);
 };
 
 // Lazy rescaling: a row's exponentials use a reference maximum m_ref and are
@@ -150,22 +169,74 @@ struct SplitCfg {
 // 2^-21 of the reference maximum. The offset cancels in acc / l.
 constexpr float kTau = 8.0f;
 constexpr float kPBias = 7.0f;
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every tile: the load returns zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int D, int RT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+// One 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
+// land at lds + 16 l (buffer_load_dwordx4 ... lds; out-of-range dwords land as
+// zeros). A plain device function, so that the host pass of the kernel
+// templates never sees the LDS address space.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// and until its LDS reads have returned, then meet the other waves at the
+// workgroup barrier. The "memory" clobber keeps the compiler from moving loads
+// or LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int D, int RT, int RG, int TP, int NS>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * pfs::kWaves, 64 * pfs::kWaves),
+                          amdgpu_waves_per_eu(SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU,
+                                              SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU))) void
 pfs_split_kernel(const SplitArgs a) {
-    using C = SplitCfg<D, RT>;
-    constexpr int KSTEPS = C::KSTEPS, CH = C::CH, LOADS = C::LOADS, MD = C::MD;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-    __shared__ float2 lds_ml[kWaves][RT * 16];
+    using C = SplitCfg<D, RT, RG, TP, NS>;
+    constexpr int KSTEPS = C::KSTEPS, KLOADS = C::KLOADS, CH = C::CH, MD = C::MD, NW = C::NW;
+    // One LDS object per stage: the compiler tracks the direct-to-LDS loads per
+    // object, so a read of one stage waits only for the loads into that stage.
+    constexpr int SB = C::STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[NS > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[NS > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st4[NS > 4 ? SB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st5[NS > 4 ? SB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st6[NS > 4 ? SB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st7[NS > 4 ? SB : 16];
+    __shared__ int64_t page_base[pfs::kPageTableEntries];  // page * page_stride + head offset
+    __shared__ float2 lds_ml[pfs::kWaves][RT * 16];
+    auto stage = [&](auto kc) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k == 0) return st0;
+        else if constexpr (k == 1) return st1;
+        else if constexpr (k == 2) return st2;
+        else if constexpr (k == 3) return st3;
+        else if constexpr (k == 4) return st4;
+        else if constexpr (k == 5) return st5;
+        else if constexpr (k == 6) return st6;
+        else return st7;
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wave % RG;  // row group: RT row tiles
+    const int tl = wave / RG;  // token lane: step tl of every stage
     const int lc = lane & 15;  // column within a 16-wide MFMA tile
     const int lg = lane >> 4;  // lane group (k-group of an operand, row-quad of a result)
 
@@ -183,28 +254,42 @@ pfs_split_kernel(const SplitArgs a) {
     const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
     const int32_t tok0 = split * a.tokens_per_split;
     if (tok0 >= L) return;  // nothing live in this split: the combine never reads it
-    const int32_t tok1 = min(tok0 + a.tokens_per_split, L);
-    const int r_begin = rb * RT * 16;
+    const int32_t tok_end = min(tok0 + a.tokens_per_split, L);
+    const int32_t nsteps = (tok_end - tok0 + kStep - 1) / kStep;
+    const int32_t nstages = (nsteps + TP - 1) / TP;
+    const int r_wave = rb * (RG * RT * 16) + rg * (RT * 16);  // first row of this wave
 
-    u32x4* q_lds = reinterpret_cast<u32x4*>(smem);
-    uint8_t* k_lds = smem + C::QBYTES + wave * 2 * C::STAGE;
-    uint8_t* v_lds = k_lds + C::STAGE;
+    // ---- page table of the split: byte offset of every page it touches ----
+    const int64_t head_off = (int64_t)g * a.head_stride;
+    {
+        const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+        const int32_t pg_first = tok0 / a.page_size;
+        const int32_t npg = min((tok_end - 1) / a.page_size - pg_first + 1, pfs::kPageTableEntries);
+        for (int e = threadIdx.x; e < npg; e += 64 * pfs::kWaves)
+            page_base[e] = (int64_t)bt_row[pg_first + e] * a.page_stride + head_off;
+    }
+    const int32_t pg_first = tok0 / a.page_size;
 
-    // ---- stage Q^T operands in LDS: slot (nt * KSTEPS + ks) * 64 + lane holds
-    //      row r_begin + 16 nt + (lane & 15), dims 64(ks/2) + 16(lane/16) + 8(ks&1) + [0, 8) ----
-    for (int slot = threadIdx.x; slot < RT * KSTEPS * 64; slot += 256) {
-        const int ln = slot & 63;
-        const int ks = (slot >> 6) % KSTEPS;
-        const int nt = (slot >> 6) / KSTEPS;
-        const int r = r_begin + nt * 16 + (ln & 15);
-        const int d0 = 64 * (ks >> 1) + 16 * (ln >> 4) + 8 * (ks & 1);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < a.rows) {
-            const int i = r / a.group;
-            const int h = a.qhead[g * a.group + (r % a.group)];
-            v = *reinterpret_cast<const u32x4*>(a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + d0);
+    // ---- Q^T operands in registers: (nt, ks) holds row r_wave + 16 nt + lc,
+    //      dims 64(ks/2) + 16 lg + 8(ks&1) + [0, 8) ----
+    f16x8 qop[RT][KSTEPS];
+#pragma unroll
+    for (int nt = 0; nt < RT; ++nt) {
+        const int r = r_wave + nt * 16 + lc;
+        const bool real = r < a.rows;
+        const int i = real ? r / a.group : 0;
+        const int h = real ? a.qhead[g * a.group + (r % a.group)] : 0;
+        const _Float16* qrow = a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D;
+#pragma unroll
+        for (int j = 0; j < KSTEPS / 2; ++j) {
+            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+            if (real) {
+                lo = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg);
+                hi = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg + 8);
+            }
+            qop[nt][2 * j] = bit_cast_<f16x8>(lo);
+            qop[nt][2 * j + 1] = bit_cast_<f16x8>(hi);
         }
-        q_lds[slot] = v;
     }
 
     // causal limit of this lane's row in each row tile: keys [0, lim) are visible.
@@ -213,11 +298,11 @@ pfs_split_kernel(const SplitArgs a) {
     int32_t lim[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
-        const int r = r_begin + nt * 16 + lc;
+        const int r = r_wave + nt * 16 + lc;
         lim[nt] = (r < a.rows) ? clamp_i((int64_t)L - a.q + r / a.group + 1, 0, L) : L;
     }
     const int32_t lim_lo = clamp_i((int64_t)L - a.q + 1, 0, L);  // smallest limit of any real row
-    const float cscale = a.sm_scale_log2e * a.kscale[g];
+    const float cscale = a.sm_scale_log2e * a.kscale[g];  // score scale, log2 domain
 
     f32x4 acc[MD][RT];
     f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
@@ -235,121 +320,141 @@ pfs_split_kernel(const SplitArgs a) {
     const f16x8 ones = f16x8{one_or_zero, one_or_zero, one_or_zero, one_or_zero,
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
-    // Load slot j of a lane: 16-byte chunk c = lane % CH of token row
-    // t_j = (64 j + lane) / CH of the 32-token step (each instruction reads
-    // 64 / CH whole rows). In LDS, row t keeps its chunks XOR-swizzled by t % CH.
-    const int ld_c = lane % CH;
-    const uint32_t ld_voff_base = 16u * (uint32_t)ld_c;
     // transposed V reads: lane j of each 16-lane block names 8 bytes of token
-    // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk
+    // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk; rows keep
+    // their chunks XOR-swizzled by token % CH
     const int tr_tok = ((lc >> 1) < 4 ? 0 : 16) + 4 * lg + ((lc >> 1) & 3);
-    const int tr_base = tr_tok * D + 8 * (lc & 1);
+    const int tr_base = C::V_OFF + tr_tok * D + 8 * (lc & 1);
     const int tr_sw = tr_tok % CH;
 
-    __syncthreads();
-
-    const int64_t head_off = (int64_t)g * a.head_stride;
-    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-    const uint32_t tile_bytes = (uint32_t)(15 * a.token_stride + D);
-    const int32_t p_begin = tok0 / kPart;
-    const int32_t p_end = (tok1 + kPart - 1) / kPart;
-    // this wave's steps: partitions p_begin + wave + 4k, two 32-token steps each
-    const int32_t nparts = (p_end - p_begin - wave + kWaves - 1) / kWaves;
-    int32_t nsteps = 0;
-    if (nparts > 0) {
-        const int32_t last_part = p_begin + wave + (nparts - 1) * kWaves;
-        nsteps = 2 * nparts - ((last_part * kPart + kStep) >= L ? 1 : 0);
+    // ---- direct-to-LDS loads. A stage holds TP steps; step s of a stage is
+    // STEP_LOADS 1 KB loads: K tile 0, K tile 1 (KLOADS each), then V rows.
+    // Lane (c, g) of K load j of a tile reads bytes [64 j + 16 g, +16) of token
+    // c: in LDS it sits exactly where that lane reads its MFMA A operand for
+    // k-steps 2j and 2j+1. V load j puts stage chunk p = 64 j + lane, which is
+    // token t = p / CH, chunk (p % CH) ^ (t % CH), at byte 16 p of the V rows.
+    // Wave (rg, tl) issues loads [rg NW, rg NW + NW) of step tl of every stage.
+    // Every 16-token tile has a buffer descriptor whose record count stops at
+    // the live length: bytes beyond it (and whole tiles past the split) land
+    // in LDS as zeros. ----
+    uint32_t voff[NW];
+    int ld_tile[NW];  // which 16-token tile each load reads (uniform)
+    bool ld_v[NW];    // V (true) or K (uniform)
+#pragma unroll
+    for (int jj = 0; jj < NW; ++jj) {
+        const int i = rg * NW + jj;
+        if (i < 2 * KLOADS) {
+            const int j = i % KLOADS;
+            ld_v[jj] = false;
+            ld_tile[jj] = i / KLOADS;
+            voff[jj] = (uint32_t)lc * (uint32_t)a.token_stride + 64u * j + 16u * lg;
+        } else {
+            const int j = i - 2 * KLOADS;
+            const int p = 64 * j + lane;
+            const int t = p / CH;
+            const int c = (p % CH) ^ (t % CH);
+            ld_v[jj] = true;
+            ld_tile[jj] = (64 * j) / CH >= 16 ? 1 : 0;
+            voff[jj] = (uint32_t)(t & 15) * (uint32_t)a.token_stride + 16u * (uint32_t)c;
+        }
     }
-    auto step_token = [&](int32_t st) -> int32_t {
-        return (p_begin + wave + (st >> 1) * kWaves) * kPart + (st & 1) * kStep;
-    };
-
-    // ---- loads of one 32-token step into registers (tokens >= L read as zeros) ----
-    u32x4 kreg[LOADS], vreg[LOADS];
-    auto load_step = [&](int32_t t_step) {
-        const bool live1 = t_step + 16 < L;
-        const int64_t off0 = (int64_t)bt_row[t_step / a.page_size] * a.page_stride +
-                             (int64_t)(t_step % a.page_size) * a.token_stride + head_off;
-        const int64_t off1 = live1 ? (int64_t)bt_row[(t_step + 16) / a.page_size] * a.page_stride +
-                                         (int64_t)((t_step + 16) % a.page_size) * a.token_stride + head_off
-                                   : 0;
-        const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(a.kpool + off0, tile_bytes);
-        const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(a.kpool + off1, tile_bytes);
-        const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(a.vpool + off0, tile_bytes);
-        const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(a.vpool + off1, tile_bytes);
+    auto issue = [&](int32_t ss, uint8_t* stg) __attribute__((always_inline)) {
+        const int32_t st = ss * TP + tl;
+        const int32_t t_step = tok0 + st * kStep;
+        int64_t off[2];
+        uint32_t rec[2];
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int t = (64 * j + lane) / CH;  // token of the step; the 16-token tile is uniform in j
-            const uint32_t voff = (t_step + t < L) ? (uint32_t)(t & 15) * (uint32_t)a.token_stride + ld_voff_base
-                                                   : kOutOfRange;
-            const bool tile1 = (64 * j) / CH >= 16;
-            kreg[j] = bit_cast_<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(tile1 ? k1 : k0, voff, 0, 0));
-            vreg[j] = bit_cast_<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(tile1 ? v1 : v0, voff, 0, 0));
+        for (int mt = 0; mt < 2; ++mt) {
+            const int32_t t0 = t_step + 16 * mt;
+            const int32_t n = (st < nsteps) ? clamp_i((int64_t)L - t0, 0, 16) : 0;
+            off[mt] = 0;
+            rec[mt] = 0;
+            if (n > 0) {
+                int32_t pg, slot;
+                if (a.page_shift >= 0) {
+                    pg = t0 >> a.page_shift;
+                    slot = t0 & (a.page_size - 1);
+                } else {
+                    pg = t0 / a.page_size;
+                    slot = t0 - pg * a.page_size;
+                }
+                const int64_t pb = page_base[min(pg - pg_first, pfs::kPageTableEntries - 1)];
+                const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)pb);
+                const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pb >> 32));
+                off[mt] = (int64_t)(((uint64_t)hi << 32) | lo) + (int64_t)slot * a.token_stride;
+                rec[mt] = (uint32_t)n * (uint32_t)a.token_stride;
+            }
+        }
+        const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(a.kpool + off[0], rec[0]);
+        const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(a.kpool + off[1], rec[1]);
+        const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(a.vpool + off[0], rec[0]);
+        const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(a.vpool + off[1], rec[1]);
+        uint8_t* dst = stg + tl * C::STEP_BYTES + 1024 * rg * NW;
+#pragma unroll
+        for (int jj = 0; jj < NW; ++jj) {
+            const __amdgpu_buffer_rsrc_t r = ld_v[jj] ? (ld_tile[jj] ? v1 : v0) : (ld_tile[jj] ? k1 : k0);
+            load_lds16(r, dst + 1024 * jj, voff[jj]);
         }
     };
 
-    if (nsteps > 0) load_step(step_token(0));
-
-    for (int32_t st = 0; st < nsteps; ++st) {
-        const int32_t t_step = step_token(st);
-        // this step's K and V -> the wave's LDS stages, then prefetch the next step
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int t = (64 * j + lane) / CH;
-            const int off = t * D + ((ld_c ^ (t % CH)) << 4);
-            *reinterpret_cast<u32x4*>(k_lds + off) = kreg[j];
-            *reinterpret_cast<u32x4*>(v_lds + off) = vreg[j];
-        }
-        if (st + 1 < nsteps) load_step(step_token(st + 1));
-
-        // ---- S^T = K * Q^T ----
+    // ---- one 32-token step from LDS; edge steps hold masked (row, token) pairs ----
+    auto step = [&](int32_t t_step, const uint8_t* sbase, bool edge) __attribute__((always_inline)) {
+        // S^T = K * Q^T. The K reads of chunk j + 1 are issued before chunk j
+        // is converted; the scheduling barriers keep the compiler from hoisting
+        // every read and conversion of the step at once (register pressure).
         f32x4 s[2][RT];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto kread = [&](int mt, int j) __attribute__((always_inline)) {
+            return *reinterpret_cast<const u32x4*>(sbase + 1024 * (mt * KLOADS + j) + 16 * lane);
+        };
+        u32x4 kn0 = kread(0, 0), kn1 = kread(1, 0);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            f16x8 qop[RT];
-#pragma unroll
-            for (int nt = 0; nt < RT; ++nt) qop[nt] = bit_cast_<f16x8>(q_lds[(nt * KSTEPS + ks) * 64 + lane]);
-            const int chunk = 4 * (ks >> 1) + lg;
+        for (int j = 0; j < KLOADS; ++j) {
+            const u32x4 kw[2] = {kn0, kn1};
+            if (j + 1 < KLOADS) {
+                kn0 = kread(0, j + 1);
+                kn1 = kread(1, j + 1);
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const int t = 16 * mt + lc;
-                const u32x2 w = *reinterpret_cast<const u32x2*>(k_lds + t * D + ((chunk ^ (t % CH)) << 4) +
-                                                                8 * (ks & 1));
-                const f16x8 kop = e4m3x8_to_f16x8(w.x, w.y);
+                const f16x8 k_lo = e4m3x8_to_f16x8(kw[mt].x, kw[mt].y);
+                const f16x8 k_hi = e4m3x8_to_f16x8(kw[mt].z, kw[mt].w);
 #pragma unroll
-                for (int nt = 0; nt < RT; ++nt)
-                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[nt], s[mt][nt], 0, 0, 0);
+                for (int nt = 0; nt < RT; ++nt) {
+                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, qop[nt][2 * j], s[mt][nt], 0, 0, 0);
+                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, qop[nt][2 * j + 1], s[mt][nt], 0, 0, 0);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- online softmax, log2 domain, lazy reference maximum ----
-        const bool edge = t_step + kStep > lim_lo;  // some (row, token) of this step is masked
+        // online softmax, log2 domain, lazy reference maximum. Scores are scaled
+        // before masking, so a masked score is exactly -inf for any finite K scale.
+        float x[RT][8];
         float smax[RT];
         bool need = false;
 #pragma unroll
+        for (int nt = 0; nt < RT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[nt][e] = s[e >> 2][nt][e & 3] * cscale;
+        if (edge) {  // uniform: only steps that cross some row's causal limit or the live length
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (t_step + (e >> 2) * 16 + 4 * lg + (e & 3) >= lim[nt]) x[nt][e] = -INFINITY;
+        }
+#pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = s[mt][nt][i];
-                    if (edge) {
-                        const int32_t t = t_step + mt * 16 + 4 * lg + i;
-                        v = (t < lim[nt]) ? v : -INFINITY;
-                        s[mt][nt][i] = v;
-                    }
-                    mx = fmaxf(mx, v);
-                }
-            mx = wave_max_xor_16_32(mx);
-            smax[nt] = mx * cscale;  // cscale > 0; -inf stays -inf
+            float mx = fmaxf(fmaxf(fmaxf(x[nt][0], x[nt][1]), fmaxf(x[nt][2], x[nt][3])),
+                             fmaxf(fmaxf(x[nt][4], x[nt][5]), fmaxf(x[nt][6], x[nt][7])));
+            smax[nt] = max_over_lane_groups(mx);
             need |= (smax[nt] > mref[nt] + kTau);
         }
-        if (__any(need)) {
+        if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) {
                 const float m_new = fmaxf(mref[nt], smax[nt]);
@@ -363,89 +468,142 @@ pfs_split_kernel(const SplitArgs a) {
                 }
             }
         }
+        // P = exp2(x - m_ref + kPBias); masked terms are exp2(-inf) = 0 (nb is
+        // finite: it only changes together with a finite m_ref)
         f16x8 pop[RT];
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            _Float16 ph[8];
+            f16x2 pp[4];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = s[mt][nt][i];
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(v, cscale, nb[nt]));
-                    ph[mt * 4 + i] = (_Float16)((edge && v == -INFINITY) ? 0.0f : pv);
-                }
-            pop[nt] = f16x8{ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(x[nt][e] + nb[nt]);
+                const float p1 = __builtin_amdgcn_exp2f(x[nt][e + 1] + nb[nt]);
+                pp[e >> 1] = f16x2{(_Float16)p0, (_Float16)p1};
+            }
+            pop[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
+                                             bit_cast_<uint32_t>(pp[2]), bit_cast_<uint32_t>(pp[3])});
         }
 
-        // ---- O^T += V^T * P^T (V^T read transposed from LDS), l += 1 * P^T ----
+        // O^T += V^T * P^T (V^T read transposed from LDS, two tiles ahead), l += 1 * P^T
+        auto vread = [&](int md) __attribute__((always_inline)) {
+            const int addr = tr_base + ((md ^ tr_sw) << 4);
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(sbase + addr));
+        };
+        i32x2 vn[2];
+        vn[0] = vread(0);
+        if (MD > 1) vn[1] = vread(1);
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-            const int addr = tr_base + ((md ^ tr_sw) << 4);
-            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(v_lds + addr));
+            const i32x2 w = vn[md & 1];
+            if (md + 2 < MD) vn[md & 1] = vread(md + 2);
             const f16x8 vop = e4m3x8_to_f16x8((uint32_t)w.x, (uint32_t)w.y);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
                 acc[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md][nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int nt = 0; nt < RT; ++nt) lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
-    }
+        for (int nt = 0; nt < RT; ++nt)
+            lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
+    };
 
-    // ---- merge the four wave states in wave order ----
-    // row sums live in result row 0 of the ones tile: lanes of lane group 0, element 0
-    if (lg == 0) {
-#pragma unroll
-        for (int nt = 0; nt < RT; ++nt) lds_ml[wave][nt * 16 + lc] = make_float2(mref[nt], lacc[nt][0]);
+    __syncthreads();  // page table ready
+
+    // ---- pipeline: NS - 1 stages in flight ahead of the one being folded ----
+    static_for<NS - 1>([&](auto kc) __attribute__((always_inline)) { issue(decltype(kc)::value, stage(kc)); });
+    for (int32_t ss0 = 0; ss0 < nstages; ss0 += NS) {
+        static_for<NS>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            const int32_t ss = ss0 + k;
+            // this wave's loads of stage ss are done once at most (NS - 2) * NW
+            // younger ones are in flight; the barrier makes every wave's loads of
+            // stage ss visible and retires every read of the stage refilled next
+            wait_vm_and_barrier<(NS - 2) * NW>();
+            issue(ss + NS - 1, stage(std::integral_constant<int, (k + NS - 1) % NS>{}));
+            const int32_t st = ss * TP + tl;
+            if (ss < nstages && st < nsteps) {
+                const int32_t t_step = tok0 + st * kStep;
+                const uint8_t* sbase = stage(kc) + tl * C::STEP_BYTES;
+                step(t_step, sbase, t_step + kStep > lim_lo);
+            }
+        });
     }
-    __syncthreads();  // every wave is also done with Q, K and V in LDS from here on
-    float M[RT], Ltot[RT];
+    wait_vm_and_barrier<0>();  // no load into LDS is still in flight
+
+    // ---- merge the TP token lanes of each row group: ((tl0 + tl2) + (tl1 + tl3)) ----
+    const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
+    float Ltot[RT];
+    if constexpr (TP == 1) {
 #pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-        float mm = -INFINITY;
+        for (int nt = 0; nt < RT; ++nt) Ltot[nt] = lacc[nt][0];  // valid in lane group 0
+    } else {
+        // row sums live in result row 0 of the ones tile: lanes of lane group 0, element 0
+        if (lg == 0) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, lds_ml[w][nt * 16 + lc].x);
-        float lt = 0.0f, fmine = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float2 ml = lds_ml[w][nt * 16 + lc];
-            const float f = (ml.x == -INFINITY) ? 0.0f : (ml.x == mm ? 1.0f : __builtin_amdgcn_exp2f(ml.x - mm));
-            lt += f * ml.y;
-            if (w == wave) fmine = f;
-        }
-        M[nt] = mm;
-        Ltot[nt] = lt;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) acc[md][nt] *= fmine;
-    }
-    u32x4* mbuf = reinterpret_cast<u32x4*>(smem);
-    for (int w = 1; w < kWaves; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt) mbuf[(md * RT + nt) * 64 + lane] = bit_cast_<u32x4>(acc[md][nt]);
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt) acc[md][nt] += bit_cast_<f32x4>(mbuf[(md * RT + nt) * 64 + lane]);
+            for (int nt = 0; nt < RT; ++nt) lds_ml[wave][nt * 16 + lc] = make_float2(mref[nt], lacc[nt][0]);
         }
         __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) {
+            float mm = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < TP; ++t) mm = fmaxf(mm, lds_ml[rg + RG * t][nt * 16 + lc].x);
+            float f[TP], lsum[TP];
+#pragma unroll
+            for (int t = 0; t < TP; ++t) {
+                const float2 ml = lds_ml[rg + RG * t][nt * 16 + lc];
+                f[t] = (ml.x == -INFINITY) ? 0.0f : (ml.x == mm ? 1.0f : __builtin_amdgcn_exp2f(ml.x - mm));
+                lsum[t] = f[t] * ml.y;
+            }
+#pragma unroll
+            for (int h = TP / 2; h >= 1; h >>= 1)
+#pragma unroll
+                for (int t = 0; t < h; ++t) lsum[t] += lsum[t + h];
+            Ltot[nt] = lsum[0];
+            float fmine = f[0];
+#pragma unroll
+            for (int t = 1; t < TP; ++t)
+                if (t == tl) fmine = f[t];
+            mref[nt] = mm;
+#pragma unroll
+            for (int md = 0; md < MD; ++md) acc[md][nt] *= fmine;
+        }
+        u32x4* mbuf = reinterpret_cast<u32x4*>(st0);
+        constexpr int MM = C::MERGE_MD;
+#pragma unroll
+        for (int h = TP / 2; h >= 1; h >>= 1) {
+#pragma unroll
+            for (int m0 = 0; m0 < MD; m0 += MM) {
+                if (tl >= h && tl < 2 * h) {
+                    const int slot = (tl - h) * RG + rg;
+#pragma unroll
+                    for (int md = m0; md < m0 + MM; ++md)
+#pragma unroll
+                        for (int nt = 0; nt < RT; ++nt)
+                            mbuf[(slot * MM * RT + (md - m0) * RT + nt) * 64 + lane] = bit_cast_<u32x4>(acc[md][nt]);
+                }
+                __syncthreads();
+                if (tl < h) {
+                    const int slot = tl * RG + rg;
+#pragma unroll
+                    for (int md = m0; md < m0 + MM; ++md)
+#pragma unroll
+                        for (int nt = 0; nt < RT; ++nt)
+                            acc[md][nt] += bit_cast_<f32x4>(mbuf[(slot * MM * RT + (md - m0) * RT + nt) * 64 + lane]);
+                }
+                __syncthreads();
+            }
+        }
+        if (tl != 0) return;
     }
-    if (wave != 0) return;
 
     // ---- emit the split partial: (reference max, sum) and the unnormalized PV ----
     // accumulator element i of d tile md is column 16 md + 4 lg + i of row r
-    const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
-        const int r = r_begin + nt * 16 + lc;
+        const int r = r_wave + nt * 16 + lc;
         if (r >= a.rows) continue;
-        if (lg == 0) reinterpret_cast<float2*>(a.ws_ml)[slot_base + r] = make_float2(M[nt], Ltot[nt]);
+        if (lg == 0) reinterpret_cast<float2*>(a.ws_ml)[slot_base + r] = make_float2(mref[nt], Ltot[nt]);
         float* dst = a.ws_acc + (slot_base + r) * D + 4 * lg;
 #pragma unroll
         for (int md = 0; md < MD; ++md) *reinterpret_cast<f32x4*>(dst + 16 * md) = acc[md][nt];
@@ -508,7 +666,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const C
 
     float mx = -INFINITY;
     for (int s = threadIdx.x; s < ns; s += 64 * kCombineWaves) mx = fmaxf(mx, ml[slot0 + s * stride].x);
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = max_over_lane_groups(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
     float M = red[0];
@@ -588,22 +747,38 @@ __global__ __launch_bounds__(256) void pfs_dequant_kernel(const uint8_t* pool, c
     dst[1] = res[1];
 }
 
-template <int D, int RT>
+template <int D, int RT, int RG>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
+    constexpr int TP = pfs::kWaves / RG;
+    constexpr int NS = pfs::split_stages(D, TP);
     const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
     const int64_t wgs = ((units + 7) / 8) * 8 * a.row_blocks;
-    hipLaunchKernelGGL((pfs_split_kernel<D, RT>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS>), dim3((unsigned)wgs), dim3(64 * pfs::kWaves), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
+// Row groups above one occur only with the most row tiles a wave can hold.
+template <int D, int RT>
+hipError_t launch_split_rt(const SplitArgs& a, int32_t row_groups, hipStream_t stream) {
+    if constexpr (RT > pfs::max_row_tiles(D)) {
+        return hipErrorInvalidValue;
+    } else {
+        if (row_groups == 1) return launch_split<D, RT, 1>(a, stream);
+        if constexpr (RT == pfs::max_row_tiles(D)) {
+            if (row_groups == 2) return launch_split<D, RT, 2>(a, stream);
+            if (row_groups == 4) return launch_split<D, RT, 4>(a, stream);
+        }
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int D>
-hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, hipStream_t stream) {
+hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t row_groups, hipStream_t stream) {
     switch (row_tiles) {
-        case 1: return launch_split<D, 1>(a, stream);
-        case 2: return launch_split<D, 2>(a, stream);
-        case 4:
-            if constexpr (pfs::max_row_tiles(D) >= 4) return launch_split<D, 4>(a, stream);
-            return hipErrorInvalidValue;
+        case 1: return launch_split_rt<D, 1>(a, row_groups, stream);
+        case 2: return launch_split_rt<D, 2>(a, row_groups, stream);
+        case 4: return launch_split_rt<D, 4>(a, row_groups, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -633,6 +808,7 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     sa.group = plan->group;
     sa.rows = plan->rows;
     sa.page_size = p.page_size;
+    sa.page_shift = (p.page_size & (p.page_size - 1)) == 0 ? __builtin_ctz((unsigned)p.page_size) : -1;
     sa.max_pages = p.max_pages_per_row;
     sa.capacity = plan->capacity;
     sa.tokens_per_split = plan->tokens_per_split;
@@ -644,9 +820,9 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     switch (p.head_dim) {
-        case 64: e = launch_split_d<64>(sa, plan->row_tiles, s); break;
-        case 128: e = launch_split_d<128>(sa, plan->row_tiles, s); break;
-        case 256: e = launch_split_d<256>(sa, plan->row_tiles, s); break;
+        case 64: e = launch_split_d<64>(sa, plan->row_tiles, plan->row_groups, s); break;
+        case 128: e = launch_split_d<128>(sa, plan->row_tiles, plan->row_groups, s); break;
+        case 256: e = launch_split_d<256>(sa, plan->row_tiles, plan->row_groups, s); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;

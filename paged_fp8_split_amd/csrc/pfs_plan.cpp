@@ -15,25 +15,27 @@ bool is_multiple(int64_t v, int64_t m) { return v % m == 0; }
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Row tiles (of 16 rows) per split workgroup: the smallest supported tile count
-// that holds all rows, capped by the accumulator budget; the rest becomes row
-// blocks along the grid.
-void choose_row_tiles(int32_t rows, int32_t head_dim, int32_t* tiles, int32_t* blocks) {
-    const int32_t max_tiles = pfs::max_row_tiles(head_dim);
-    static const int32_t kTiles[] = {1, 2, 4};
-    int32_t need = (rows + 15) / 16;
-    if (need > max_tiles) {
-        *tiles = max_tiles;
-        *blocks = (rows + 16 * max_tiles - 1) / (16 * max_tiles);
-        return;
-    }
-    for (int32_t t : kTiles) {
-        if (t >= need) {
-            *tiles = t;
-            break;
-        }
-    }
-    *blocks = 1;
+int32_t pow2_ceil(int32_t v) {
+    int32_t p = 1;
+    while (p < v) p *= 2;
+    return p;
+}
+
+// Shape of the split workgroups: each wave folds RT 16-row tiles; RG waves
+// cover the rows (row groups) and the remaining 4 / RG waves take alternate
+// 32-token steps (token lanes). Tiles per wave come first: every wave converts
+// the E4M3 bytes it reads, so more rows per wave means fewer conversions per
+// row. Rows beyond RT * RG tiles become row blocks of the grid.
+void choose_split_shape(int32_t rows, int32_t head_dim, pfs_plan* plan) {
+    const int32_t tiles = (rows + 15) / 16 > 0 ? (rows + 15) / 16 : 1;
+    const int32_t max_rt = pfs::max_row_tiles(head_dim);
+    const int32_t rt = pow2_ceil(tiles) < max_rt ? pow2_ceil(tiles) : max_rt;
+    const int32_t groups = pow2_ceil((tiles + rt - 1) / rt);
+    const int32_t rg = groups < pfs::kWaves ? groups : pfs::kWaves;
+    plan->row_tiles = rt;
+    plan->row_groups = rg;
+    plan->token_lanes = pfs::kWaves / rg;
+    plan->row_blocks = (tiles + rt * rg - 1) / (rt * rg);
 }
 
 }  // namespace
@@ -118,18 +120,30 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
             plan->qhead[g * G + fill[g]++] = (uint8_t)h;
         }
     }
-    choose_row_tiles(plan->rows, p.head_dim, &plan->row_tiles, &plan->row_blocks);
+    choose_split_shape(plan->rows, p.head_dim, plan);
 
     // Split length: a pure function of the shape (never of device data), so a
     // plan always folds the same partitions in the same order.
+    // A split's pages must fit the kernel's LDS page table (a split of tps
+    // tokens starting on a partition boundary touches at most tps / page + 2).
+    const int64_t max_tps = (int64_t)(pfs::kPageTableEntries - 2) * p.page_size / pfs::kPartitionTokens *
+                            pfs::kPartitionTokens;
     int64_t tps = p.tokens_per_split;
+    if (tps > max_tps) {
+        delete plan;
+        return PFS_ERR_UNSUPPORTED;
+    }
     if (tps == 0) {
+        const int32_t stages = pfs::split_stages(p.head_dim, plan->token_lanes);
+        const int64_t per_cu = pfs::split_workgroups_per_cu(p.head_dim, plan->token_lanes, stages);
+        const int64_t target = pfs::kDefaultTargetWorkgroups / 2 * per_cu;  // 256 CUs
         const int64_t units = (int64_t)(p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->row_blocks;
-        int64_t splits = (pfs::kDefaultTargetWorkgroups + units - 1) / units;
+        int64_t splits = (target + units - 1) / units;
         if (splits < 1) splits = 1;
         tps = round_up((capacity + splits - 1) / splits, pfs::kPartitionTokens);
-        const int64_t min_tps = (int64_t)pfs::kWaves * pfs::kPartitionTokens;  // one partition per wave
+        const int64_t min_tps = (int64_t)pfs::kWaves * pfs::kPartitionTokens;
         if (tps < min_tps) tps = min_tps;
+        if (tps > max_tps) tps = max_tps;
     }
     if (tps > round_up(capacity, pfs::kPartitionTokens)) tps = round_up(capacity, pfs::kPartitionTokens);
     plan->tokens_per_split = (int32_t)tps;
