@@ -9,31 +9,37 @@
 namespace pfs {
 
 constexpr int kPartitionTokens = 64;  // the K64 partition: unit of work and of ordering
-constexpr int kWaves = 4;             // waves per split workgroup
 constexpr int kMaxQHeads = 256;
 constexpr int kMaxQ = 16;
 // 16-row MFMA tiles per wave of the split kernel. Each wave keeps its FP32
 // accumulators (16 RT rows x head_dim) and its Q^T operands in VGPRs; the cap
 // keeps that, with the step's operands, within 256 VGPRs (two waves per SIMD).
 constexpr int max_row_tiles(int head_dim) { return head_dim >= 256 ? 1 : (head_dim >= 128 ? 2 : 4); }
-constexpr int kDefaultTargetWorkgroups = 512;
-// Pages one split workgroup can address: their byte offsets sit in LDS.
-constexpr int kPageTableEntries = 1024;
+// Byte offsets of the 16-token tiles of one split sit in an LDS table.
+constexpr int kTileTableEntries = 1024;
+constexpr int kMaxTokensPerSplit = 16 * kTileTableEntries;
+constexpr int kCUs = 256;  // MI355X compute units
 
-// LDS of one split stage: TP 32-token steps of K and V bytes.
+// A split workgroup has W = RG * TP waves: RG row groups (RT row tiles each)
+// times TP token lanes; a stage holds TP 32-token steps of K and V bytes.
 constexpr int split_stage_bytes(int head_dim, int token_lanes) { return token_lanes * 64 * head_dim; }
-// Stages in flight: up to 64 KB of stages when two workgroups fit a CU,
-// otherwise up to 128 KB for one workgroup per CU.
-constexpr int split_stages(int head_dim, int token_lanes) {
-    const int s = split_stage_bytes(head_dim, token_lanes);
-    if (s <= 16384) {
-        const int n = 65536 / s;
-        return n >= 8 ? 8 : (n >= 4 ? 4 : 2);
-    }
-    return 131072 / s >= 4 ? 4 : 2;
+// Eight waves whenever a stage of 8 / RG steps stays within 64 KB.
+constexpr int split_waves(int head_dim, int row_groups) {
+    return split_stage_bytes(head_dim, 8 / row_groups) <= 65536 ? 8 : 4;
 }
-constexpr int split_workgroups_per_cu(int head_dim, int token_lanes, int stages) {
-    return split_stage_bytes(head_dim, token_lanes) * stages <= 65536 ? 2 : 1;
+// Four-wave workgroups with small stages run two per CU (64 KB of stages
+// each); every other shape runs one per CU with up to 128 KB of stages.
+constexpr int split_stages(int head_dim, int token_lanes, int waves) {
+    const int s = split_stage_bytes(head_dim, token_lanes);
+    const int budget = (waves == 4 && s <= 16384) ? 65536 : 131072;
+    const int n = budget / s;
+    return n >= 8 ? 8 : (n >= 4 ? 4 : 2);
+}
+constexpr int split_workgroups_per_cu(int head_dim, int token_lanes, int waves) {
+    return (waves == 4 && split_stage_bytes(head_dim, token_lanes) * split_stages(head_dim, token_lanes, waves) <=
+                              65536)
+               ? 2
+               : 1;
 }
 
 }  // namespace pfs
@@ -44,7 +50,8 @@ struct pfs_plan {
     int32_t rows;            // rows per (request, KV head): R = G * q; row r = i * G + jj
     int32_t row_tiles;       // 16-row tiles per wave (template parameter)
     int32_t row_groups;      // waves along the rows of a workgroup (template parameter)
-    int32_t token_lanes;     // waves along the tokens of a workgroup: kWaves / row_groups
+    int32_t token_lanes;     // waves along the tokens of a workgroup
+    int32_t waves;           // waves per split workgroup: row_groups * token_lanes
     int32_t row_blocks;      // workgroups along the rows of one (request, KV head)
     int32_t capacity;        // block-table row capacity in tokens
     int32_t tokens_per_split;

@@ -135,31 +135,31 @@ struct SplitArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// Compile-time geometry of the split kernel: RT 16-row tiles per wave, RG row
-// groups x TP token lanes = 4 waves, NS LDS stages of TP 32-token steps.
+// Compile-time geometry of the split kernel: W = RG * TP waves (RG row groups
+// of RT 16-row tiles, TP token lanes), NS LDS stages of TP 32-token steps.
 template <int D, int RT, int RG, int TP, int NS>
 struct SplitCfg {
     static constexpr int W = RG * TP;
-    static_assert(W == pfs::kWaves, "four waves per split workgroup");
+    static_assert(W == 4 || W == 8, "four or eight waves per split workgroup");
     static constexpr int KSTEPS = D / 32;           // QK k-steps (32 dims each)
     static constexpr int KLOADS = D / 64;           // 1 KB loads per 16-token K tile
     static constexpr int CH = D / 16;               // 16-byte chunks per token row
     static constexpr int MD = D / 16;               // PV tiles along head_dim
+    static constexpr int SWB = CH < 8 ? CH : 8;     // values of the V chunk swizzle
     static constexpr int STEP_LOADS = D / 16;       // 1 KB loads per 32-token step: K tile 0, K tile 1, V
     static constexpr int STEP_BYTES = 1024 * STEP_LOADS;
     static constexpr int V_OFF = 1024 * (D / 32);   // V rows within a step
     static constexpr int STAGE_BYTES = TP * STEP_BYTES;
     static constexpr int NW = STEP_LOADS / RG;      // loads per wave per stage
-    static constexpr int ACC_SLOTS = MD * RT * 64;  // 16-byte slots of one wave's accumulators
     // md tiles merged per round so that one tree level of writers fits in stage 0
-    static constexpr int MERGE_MD = TP > 1 ? (STAGE_BYTES / (RG * (TP / 2) * RT * 1024) < MD
-                                                  ? STAGE_BYTES / (RG * (TP / 2) * RT * 1024)
-                                                  : MD)
-                                           : MD;
-    static_assert(TP == 1 || (MERGE_MD >= 1 && MD % MERGE_MD == 0), "merge chunking");
+    static constexpr int MERGE_DIV = RG * (TP > 1 ? TP / 2 : 1) * RT * 1024;
+    static constexpr bool MERGE_IN_STAGE = STAGE_BYTES >= MERGE_DIV;  // else a buffer of its own
+    static constexpr int MERGE_MD =
+        MERGE_IN_STAGE ? (STAGE_BYTES / MERGE_DIV < MD ? STAGE_BYTES / MERGE_DIV : MD) : 1;
+    static constexpr int MERGE_EXTRA_BYTES = (TP > 1 && !MERGE_IN_STAGE) ? MERGE_DIV : 16;
+    static_assert(TP == 1 || MD % MERGE_MD == 0, "merge chunking");
     static_assert(NS == 2 || NS == 4 || NS == 8, "stages");
-    static constexpr int LDS_BYTES = NS * STAGE_BYTES + 8 * pfs::kPageTableEntries;
-    static constexpr int WAVES_PER_EU = pfs::split_workgroups_per_cu(D, TP, NS);
+    static constexpr int WAVES_PER_EU = W * pfs::split_workgroups_per_cu(D, TP, W) / 4;
 };
 
 // Lazy rescaling: a row's exponentials use a reference maximum m_ref and are
@@ -182,6 +182,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
+// Transposed 8-byte LDS read (ds_read_b64_tr_b8) at lds + byte offset.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* lds) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(lds));
+}
+
 template <typename F, int... Is>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
     (f(std::integral_constant<int, Is>{}), ...);
@@ -201,13 +206,19 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Swizzle of the 16-byte V chunks of token t (row t of a step): chunk c sits at
+// chunk position c ^ swz(t). The 8 tokens one 16-lane block reads in a
+// transposed read get distinct values, so the block hits distinct banks.
+__device__ __forceinline__ int v_swizzle(int t, int swb) { return ((t & 3) | ((t >> 4) << 2)) & (swb - 1); }
+
 template <int D, int RT, int RG, int TP, int NS>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * pfs::kWaves, 64 * pfs::kWaves),
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * RG * TP, 64 * RG * TP),
                           amdgpu_waves_per_eu(SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU,
                                               SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU))) void
 pfs_split_kernel(const SplitArgs a) {
     using C = SplitCfg<D, RT, RG, TP, NS>;
-    constexpr int KSTEPS = C::KSTEPS, KLOADS = C::KLOADS, CH = C::CH, MD = C::MD, NW = C::NW;
+    constexpr int W = C::W, KSTEPS = C::KSTEPS, KLOADS = C::KLOADS, CH = C::CH, MD = C::MD, NW = C::NW;
+    constexpr int SWB = C::SWB;
     // One LDS object per stage: the compiler tracks the direct-to-LDS loads per
     // object, so a read of one stage waits only for the loads into that stage.
     constexpr int SB = C::STAGE_BYTES;
@@ -219,8 +230,9 @@ pfs_split_kernel(const SplitArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t st5[NS > 4 ? SB : 16];
     __shared__ __attribute__((aligned(16))) uint8_t st6[NS > 4 ? SB : 16];
     __shared__ __attribute__((aligned(16))) uint8_t st7[NS > 4 ? SB : 16];
-    __shared__ int64_t page_base[pfs::kPageTableEntries];  // page * page_stride + head offset
-    __shared__ float2 lds_ml[pfs::kWaves][RT * 16];
+    __shared__ int64_t tile_off[pfs::kTileTableEntries];  // pool byte offset of every 16-token tile of the split
+    __shared__ float2 lds_ml[W][RT * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t merge_extra[C::MERGE_EXTRA_BYTES];
     auto stage = [&](auto kc) __attribute__((always_inline)) -> uint8_t* {
         constexpr int k = decltype(kc)::value;
         if constexpr (k == 0) return st0;
@@ -259,16 +271,18 @@ pfs_split_kernel(const SplitArgs a) {
     const int32_t nstages = (nsteps + TP - 1) / TP;
     const int r_wave = rb * (RG * RT * 16) + rg * (RT * 16);  // first row of this wave
 
-    // ---- page table of the split: byte offset of every page it touches ----
-    const int64_t head_off = (int64_t)g * a.head_stride;
+    // ---- tile table: pool byte offset of every 16-token tile of the split ----
     {
+        const int64_t head_off = (int64_t)g * a.head_stride;
         const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-        const int32_t pg_first = tok0 / a.page_size;
-        const int32_t npg = min((tok_end - 1) / a.page_size - pg_first + 1, pfs::kPageTableEntries);
-        for (int e = threadIdx.x; e < npg; e += 64 * pfs::kWaves)
-            page_base[e] = (int64_t)bt_row[pg_first + e] * a.page_stride + head_off;
+        const int32_t ntiles = min((tok_end - tok0 + 15) / 16, pfs::kTileTableEntries);
+        for (int e = threadIdx.x; e < ntiles; e += 64 * W) {
+            const int32_t t0 = tok0 + 16 * e;
+            const int32_t pg = t0 / a.page_size;
+            const int32_t slot = t0 - pg * a.page_size;
+            tile_off[e] = (int64_t)bt_row[pg] * a.page_stride + (int64_t)slot * a.token_stride + head_off;
+        }
     }
-    const int32_t pg_first = tok0 / a.page_size;
 
     // ---- Q^T operands in registers: (nt, ks) holds row r_wave + 16 nt + lc,
     //      dims 64(ks/2) + 16 lg + 8(ks&1) + [0, 8) ----
@@ -321,18 +335,22 @@ pfs_split_kernel(const SplitArgs a) {
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
     // transposed V reads: lane j of each 16-lane block names 8 bytes of token
-    // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk; rows keep
-    // their chunks XOR-swizzled by token % CH
+    // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk. With
+    // the chunk swizzle below SWB, tile md sits at vaddr[md % SWB] + 16 SWB (md / SWB).
     const int tr_tok = ((lc >> 1) < 4 ? 0 : 16) + 4 * lg + ((lc >> 1) & 3);
-    const int tr_base = C::V_OFF + tr_tok * D + 8 * (lc & 1);
-    const int tr_sw = tr_tok % CH;
+    // Both read addresses include this token lane's step within the stage.
+    int vaddr[SWB];
+#pragma unroll
+    for (int m = 0; m < SWB; ++m)
+        vaddr[m] = tl * C::STEP_BYTES + C::V_OFF + tr_tok * D + 8 * (lc & 1) + 16 * (m ^ v_swizzle(tr_tok, SWB));
+    const int kaddr = tl * C::STEP_BYTES + 16 * lane;
 
     // ---- direct-to-LDS loads. A stage holds TP steps; step s of a stage is
     // STEP_LOADS 1 KB loads: K tile 0, K tile 1 (KLOADS each), then V rows.
     // Lane (c, g) of K load j of a tile reads bytes [64 j + 16 g, +16) of token
     // c: in LDS it sits exactly where that lane reads its MFMA A operand for
     // k-steps 2j and 2j+1. V load j puts stage chunk p = 64 j + lane, which is
-    // token t = p / CH, chunk (p % CH) ^ (t % CH), at byte 16 p of the V rows.
+    // token t = p / CH, chunk (p % CH) ^ swz(t), at byte 16 p of the V rows.
     // Wave (rg, tl) issues loads [rg NW, rg NW + NW) of step tl of every stage.
     // Every 16-token tile has a buffer descriptor whose record count stops at
     // the live length: bytes beyond it (and whole tiles past the split) land
@@ -340,6 +358,7 @@ pfs_split_kernel(const SplitArgs a) {
     uint32_t voff[NW];
     int ld_tile[NW];  // which 16-token tile each load reads (uniform)
     bool ld_v[NW];    // V (true) or K (uniform)
+    int tile_mask = 0;
 #pragma unroll
     for (int jj = 0; jj < NW; ++jj) {
         const int i = rg * NW + jj;
@@ -352,52 +371,40 @@ pfs_split_kernel(const SplitArgs a) {
             const int j = i - 2 * KLOADS;
             const int p = 64 * j + lane;
             const int t = p / CH;
-            const int c = (p % CH) ^ (t % CH);
+            const int c = (p % CH) ^ v_swizzle(t, SWB);
             ld_v[jj] = true;
             ld_tile[jj] = (64 * j) / CH >= 16 ? 1 : 0;
             voff[jj] = (uint32_t)(t & 15) * (uint32_t)a.token_stride + 16u * (uint32_t)c;
         }
+        tile_mask |= 1 << ld_tile[jj];
     }
     auto issue = [&](int32_t ss, uint8_t* stg) __attribute__((always_inline)) {
         const int32_t st = ss * TP + tl;
         const int32_t t_step = tok0 + st * kStep;
-        int64_t off[2];
-        uint32_t rec[2];
+        uint64_t off[2] = {0u, 0u};  // tile byte offsets in the pools (0 for an empty tile)
+        uint32_t rec[2] = {0u, 0u};  // record counts: live bytes of the tile
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const int32_t t0 = t_step + 16 * mt;
-            const int32_t n = (st < nsteps) ? clamp_i((int64_t)L - t0, 0, 16) : 0;
-            off[mt] = 0;
-            rec[mt] = 0;
+            if (!(tile_mask & (1 << mt))) continue;
+            const int32_t n = (st < nsteps) ? min(max(L - (t_step + 16 * mt), 0), 16) : 0;
             if (n > 0) {
-                int32_t pg, slot;
-                if (a.page_shift >= 0) {
-                    pg = t0 >> a.page_shift;
-                    slot = t0 & (a.page_size - 1);
-                } else {
-                    pg = t0 / a.page_size;
-                    slot = t0 - pg * a.page_size;
-                }
-                const int64_t pb = page_base[min(pg - pg_first, pfs::kPageTableEntries - 1)];
-                const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)pb);
-                const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pb >> 32));
-                off[mt] = (int64_t)(((uint64_t)hi << 32) | lo) + (int64_t)slot * a.token_stride;
+                const int64_t o = tile_off[2 * st + mt];
+                const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)o);
+                const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)o >> 32));
+                off[mt] = ((uint64_t)hi << 32) | lo;
                 rec[mt] = (uint32_t)n * (uint32_t)a.token_stride;
             }
         }
-        const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(a.kpool + off[0], rec[0]);
-        const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(a.kpool + off[1], rec[1]);
-        const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(a.vpool + off[0], rec[0]);
-        const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(a.vpool + off[1], rec[1]);
         uint8_t* dst = stg + tl * C::STEP_BYTES + 1024 * rg * NW;
 #pragma unroll
         for (int jj = 0; jj < NW; ++jj) {
-            const __amdgpu_buffer_rsrc_t r = ld_v[jj] ? (ld_tile[jj] ? v1 : v0) : (ld_tile[jj] ? k1 : k0);
-            load_lds16(r, dst + 1024 * jj, voff[jj]);
+            const int mt = ld_tile[jj];
+            const uint8_t* pool = ld_v[jj] ? a.vpool : a.kpool;
+            load_lds16(tile_rsrc(pool + off[mt], rec[mt]), dst + 1024 * jj, voff[jj]);
         }
     };
 
-    // ---- one 32-token step from LDS; edge steps hold masked (row, token) pairs ----
+    // ---- one 32-token step from stage sbase; edge steps hold masked (row, token) pairs ----
     auto step = [&](int32_t t_step, const uint8_t* sbase, bool edge) __attribute__((always_inline)) {
         // S^T = K * Q^T. The K reads of chunk j + 1 are issued before chunk j
         // is converted; the scheduling barriers keep the compiler from hoisting
@@ -408,7 +415,7 @@ pfs_split_kernel(const SplitArgs a) {
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto kread = [&](int mt, int j) __attribute__((always_inline)) {
-            return *reinterpret_cast<const u32x4*>(sbase + 1024 * (mt * KLOADS + j) + 16 * lane);
+            return *reinterpret_cast<const u32x4*>(sbase + kaddr + 1024 * (mt * KLOADS + j));
         };
         u32x4 kn0 = kread(0, 0), kn1 = kread(1, 0);
 #pragma unroll
@@ -433,24 +440,24 @@ pfs_split_kernel(const SplitArgs a) {
 
         // online softmax, log2 domain, lazy reference maximum. Scores are scaled
         // before masking, so a masked score is exactly -inf for any finite K scale.
-        float x[RT][8];
+        float xs[RT][8];
         float smax[RT];
         bool need = false;
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[nt][e] = s[e >> 2][nt][e & 3] * cscale;
+            for (int e = 0; e < 8; ++e) xs[nt][e] = s[e >> 2][nt][e & 3] * cscale;
         if (edge) {  // uniform: only steps that cross some row's causal limit or the live length
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (t_step + (e >> 2) * 16 + 4 * lg + (e & 3) >= lim[nt]) x[nt][e] = -INFINITY;
+                    if (t_step + (e >> 2) * 16 + 4 * lg + (e & 3) >= lim[nt]) xs[nt][e] = -INFINITY;
         }
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            float mx = fmaxf(fmaxf(fmaxf(x[nt][0], x[nt][1]), fmaxf(x[nt][2], x[nt][3])),
-                             fmaxf(fmaxf(x[nt][4], x[nt][5]), fmaxf(x[nt][6], x[nt][7])));
+            const float mx = fmaxf(fmaxf(fmaxf(xs[nt][0], xs[nt][1]), fmaxf(xs[nt][2], xs[nt][3])),
+                                   fmaxf(fmaxf(xs[nt][4], xs[nt][5]), fmaxf(xs[nt][6], xs[nt][7])));
             smax[nt] = max_over_lane_groups(mx);
             need |= (smax[nt] > mref[nt] + kTau);
         }
@@ -476,8 +483,8 @@ pfs_split_kernel(const SplitArgs a) {
             f16x2 pp[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(x[nt][e] + nb[nt]);
-                const float p1 = __builtin_amdgcn_exp2f(x[nt][e + 1] + nb[nt]);
+                const float p0 = __builtin_amdgcn_exp2f(xs[nt][e] + nb[nt]);
+                const float p1 = __builtin_amdgcn_exp2f(xs[nt][e + 1] + nb[nt]);
                 pp[e >> 1] = f16x2{(_Float16)p0, (_Float16)p1};
             }
             pop[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
@@ -486,8 +493,7 @@ pfs_split_kernel(const SplitArgs a) {
 
         // O^T += V^T * P^T (V^T read transposed from LDS, two tiles ahead), l += 1 * P^T
         auto vread = [&](int md) __attribute__((always_inline)) {
-            const int addr = tr_base + ((md ^ tr_sw) << 4);
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(sbase + addr));
+            return lds_read_tr8(sbase + vaddr[md % SWB] + 16 * SWB * (md / SWB));
         };
         i32x2 vn[2];
         vn[0] = vread(0);
@@ -507,7 +513,7 @@ pfs_split_kernel(const SplitArgs a) {
             lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
     };
 
-    __syncthreads();  // page table ready
+    __syncthreads();  // tile table ready
 
     // ---- pipeline: NS - 1 stages in flight ahead of the one being folded ----
     static_for<NS - 1>([&](auto kc) __attribute__((always_inline)) { issue(decltype(kc)::value, stage(kc)); });
@@ -523,14 +529,13 @@ pfs_split_kernel(const SplitArgs a) {
             const int32_t st = ss * TP + tl;
             if (ss < nstages && st < nsteps) {
                 const int32_t t_step = tok0 + st * kStep;
-                const uint8_t* sbase = stage(kc) + tl * C::STEP_BYTES;
-                step(t_step, sbase, t_step + kStep > lim_lo);
+                step(t_step, stage(kc), t_step + kStep > lim_lo);
             }
         });
     }
     wait_vm_and_barrier<0>();  // no load into LDS is still in flight
 
-    // ---- merge the TP token lanes of each row group: ((tl0 + tl2) + (tl1 + tl3)) ----
+    // ---- merge the TP token lanes of each row group: ((tl0 + tl2) + (tl1 + tl3)) ... ----
     const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
     float Ltot[RT];
     if constexpr (TP == 1) {
@@ -568,7 +573,7 @@ pfs_split_kernel(const SplitArgs a) {
 #pragma unroll
             for (int md = 0; md < MD; ++md) acc[md][nt] *= fmine;
         }
-        u32x4* mbuf = reinterpret_cast<u32x4*>(st0);
+        u32x4* mbuf = reinterpret_cast<u32x4*>(C::MERGE_IN_STAGE ? st0 : merge_extra);
         constexpr int MM = C::MERGE_MD;
 #pragma unroll
         for (int h = TP / 2; h >= 1; h >>= 1) {
@@ -749,12 +754,12 @@ __global__ __launch_bounds__(256) void pfs_dequant_kernel(const uint8_t* pool, c
 
 template <int D, int RT, int RG>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
-    constexpr int TP = pfs::kWaves / RG;
-    constexpr int NS = pfs::split_stages(D, TP);
+    constexpr int W = pfs::split_waves(D, RG);
+    constexpr int TP = W / RG;
+    constexpr int NS = pfs::split_stages(D, TP, W);
     const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
     const int64_t wgs = ((units + 7) / 8) * 8 * a.row_blocks;
-    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS>), dim3((unsigned)wgs), dim3(64 * pfs::kWaves), 0, stream,
-                       a);
+    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS>), dim3((unsigned)wgs), dim3(64 * W), 0, stream, a);
     return hipGetLastError();
 }
 

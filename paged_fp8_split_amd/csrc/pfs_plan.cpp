@@ -22,7 +22,7 @@ int32_t pow2_ceil(int32_t v) {
 }
 
 // Shape of the split workgroups: each wave folds RT 16-row tiles; RG waves
-// cover the rows (row groups) and the remaining 4 / RG waves take alternate
+// cover the rows (row groups) and TP waves per row group take alternate
 // 32-token steps (token lanes). Tiles per wave come first: every wave converts
 // the E4M3 bytes it reads, so more rows per wave means fewer conversions per
 // row. Rows beyond RT * RG tiles become row blocks of the grid.
@@ -31,10 +31,11 @@ void choose_split_shape(int32_t rows, int32_t head_dim, pfs_plan* plan) {
     const int32_t max_rt = pfs::max_row_tiles(head_dim);
     const int32_t rt = pow2_ceil(tiles) < max_rt ? pow2_ceil(tiles) : max_rt;
     const int32_t groups = pow2_ceil((tiles + rt - 1) / rt);
-    const int32_t rg = groups < pfs::kWaves ? groups : pfs::kWaves;
+    const int32_t rg = groups < 4 ? groups : 4;
     plan->row_tiles = rt;
     plan->row_groups = rg;
-    plan->token_lanes = pfs::kWaves / rg;
+    plan->waves = pfs::split_waves(head_dim, rg);
+    plan->token_lanes = plan->waves / rg;
     plan->row_blocks = (tiles + rt * rg - 1) / (rt * rg);
 }
 
@@ -124,24 +125,21 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
 
     // Split length: a pure function of the shape (never of device data), so a
     // plan always folds the same partitions in the same order.
-    // A split's pages must fit the kernel's LDS page table (a split of tps
-    // tokens starting on a partition boundary touches at most tps / page + 2).
-    const int64_t max_tps = (int64_t)(pfs::kPageTableEntries - 2) * p.page_size / pfs::kPartitionTokens *
-                            pfs::kPartitionTokens;
+    // A split's 16-token tiles must fit the kernel's LDS tile table.
+    const int64_t max_tps = pfs::kMaxTokensPerSplit;
     int64_t tps = p.tokens_per_split;
     if (tps > max_tps) {
         delete plan;
         return PFS_ERR_UNSUPPORTED;
     }
     if (tps == 0) {
-        const int32_t stages = pfs::split_stages(p.head_dim, plan->token_lanes);
-        const int64_t per_cu = pfs::split_workgroups_per_cu(p.head_dim, plan->token_lanes, stages);
-        const int64_t target = pfs::kDefaultTargetWorkgroups / 2 * per_cu;  // 256 CUs
+        const int64_t per_cu = pfs::split_workgroups_per_cu(p.head_dim, plan->token_lanes, plan->waves);
+        const int64_t target = (int64_t)pfs::kCUs * per_cu;  // one resident round of workgroups
         const int64_t units = (int64_t)(p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->row_blocks;
         int64_t splits = (target + units - 1) / units;
         if (splits < 1) splits = 1;
         tps = round_up((capacity + splits - 1) / splits, pfs::kPartitionTokens);
-        const int64_t min_tps = (int64_t)pfs::kWaves * pfs::kPartitionTokens;
+        const int64_t min_tps = 4 * (int64_t)pfs::kPartitionTokens;
         if (tps < min_tps) tps = min_tps;
         if (tps > max_tps) tps = max_tps;
     }
