@@ -263,7 +263,7 @@ pfs_split_kernel(const SplitArgs a) {
     const int g = (unit / a.num_splits) % a.num_kv_heads;
     const int b = unit / (a.num_splits * a.num_kv_heads);
 
-    const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
+    const int32_t L = __builtin_amdgcn_readfirstlane(clamp_i(a.live_len[b], 0, a.capacity));
     const int32_t tok0 = split * a.tokens_per_split;
     if (tok0 >= L) return;  // nothing live in this split: the combine never reads it
     const int32_t tok_end = min(tok0 + a.tokens_per_split, L);
@@ -346,107 +346,150 @@ pfs_split_kernel(const SplitArgs a) {
     const int kaddr = tl * C::STEP_BYTES + 16 * lane;
 
     // ---- direct-to-LDS loads. A stage holds TP steps; step s of a stage is
-    // STEP_LOADS 1 KB loads: K tile 0, K tile 1 (KLOADS each), then V rows.
-    // Lane (c, g) of K load j of a tile reads bytes [64 j + 16 g, +16) of token
-    // c: in LDS it sits exactly where that lane reads its MFMA A operand for
-    // k-steps 2j and 2j+1. V load j puts stage chunk p = 64 j + lane, which is
-    // token t = p / CH, chunk (p % CH) ^ swz(t), at byte 16 p of the V rows.
-    // Wave (rg, tl) issues loads [rg NW, rg NW + NW) of step tl of every stage.
+    // STEP_LOADS 1 KB loads in four groups of G = D / 64: K tile 0, K tile 1,
+    // V tile 0, V tile 1 (load i = group * G + jg at byte 1024 i of the step).
+    // Lane (c, g) of K load jg of a tile reads bytes [64 jg + 16 g, +16) of
+    // token c: in LDS it sits exactly where that lane reads its MFMA A operand
+    // for k-steps 2jg and 2jg+1. V load j = i - 2G puts stage chunk
+    // p = 64 j + lane, which is token t = p / CH, chunk (p % CH) ^ swz(t), at
+    // byte 16 p of the V rows. Each wave issues NW loads of step tl of every
+    // stage: when RG divides G, loads [rg G/RG, (rg+1) G/RG) of every group
+    // (pool and tile fixed per load); otherwise loads [rg NW, rg NW + NW).
     // Every 16-token tile has a buffer descriptor whose record count stops at
     // the live length: bytes beyond it (and whole tiles past the split) land
     // in LDS as zeros. ----
+    constexpr int G = D / 64;
+    constexpr bool BY_GROUP = (G % RG) == 0;
+    constexpr int PG = BY_GROUP ? G / RG : 1;  // loads per group per wave
     uint32_t voff[NW];
-    int ld_tile[NW];  // which 16-token tile each load reads (uniform)
-    bool ld_v[NW];    // V (true) or K (uniform)
-    int tile_mask = 0;
+    int ld_dst[NW];   // byte offset of each load in the step (uniform)
+    int ld_group[NW]; // group of each load (compile-time when BY_GROUP)
 #pragma unroll
     for (int jj = 0; jj < NW; ++jj) {
-        const int i = rg * NW + jj;
-        if (i < 2 * KLOADS) {
-            const int j = i % KLOADS;
-            ld_v[jj] = false;
-            ld_tile[jj] = i / KLOADS;
-            voff[jj] = (uint32_t)lc * (uint32_t)a.token_stride + 64u * j + 16u * lg;
+        int group, jg;
+        if constexpr (BY_GROUP) {
+            group = jj / PG;
+            jg = rg * PG + jj % PG;
         } else {
-            const int j = i - 2 * KLOADS;
-            const int p = 64 * j + lane;
+            const int i = rg * NW + jj;
+            group = i / G;
+            jg = i % G;
+        }
+        ld_group[jj] = group;
+        ld_dst[jj] = 1024 * (group * G + jg);
+        if (group < 2) {
+            voff[jj] = (uint32_t)lc * (uint32_t)a.token_stride + 64u * jg + 16u * lg;
+        } else {
+            const int p = 64 * ((group - 2) * G + jg) + lane;
             const int t = p / CH;
             const int c = (p % CH) ^ v_swizzle(t, SWB);
-            ld_v[jj] = true;
-            ld_tile[jj] = (64 * j) / CH >= 16 ? 1 : 0;
             voff[jj] = (uint32_t)(t & 15) * (uint32_t)a.token_stride + 16u * (uint32_t)c;
         }
-        tile_mask |= 1 << ld_tile[jj];
     }
-    auto issue = [&](int32_t ss, uint8_t* stg) __attribute__((always_inline)) {
+    // Loads of a stage are prepared one stage ahead: the tile offsets come from
+    // the LDS table (a read whose latency hides behind a fold) and the record
+    // counts from the live length.
+    struct Pending {
+        uint32_t off_lo[2], off_hi[2];  // tile byte offsets (VGPRs, uniform values)
+        int32_t n[2];                   // live tokens of each tile
+    };
+    auto prep = [&](int32_t ss) __attribute__((always_inline)) -> Pending {
+        Pending pd;
         const int32_t st = ss * TP + tl;
         const int32_t t_step = tok0 + st * kStep;
-        uint64_t off[2] = {0u, 0u};  // tile byte offsets in the pools (0 for an empty tile)
-        uint32_t rec[2] = {0u, 0u};  // record counts: live bytes of the tile
+        const int32_t e = min(2 * st, pfs::kTileTableEntries - 2);
+        const u32x2 o0 = *reinterpret_cast<const u32x2*>(&tile_off[e]);
+        const u32x2 o1 = *reinterpret_cast<const u32x2*>(&tile_off[e + 1]);
+        pd.off_lo[0] = o0.x;
+        pd.off_hi[0] = o0.y;
+        pd.off_lo[1] = o1.x;
+        pd.off_hi[1] = o1.y;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            pd.n[mt] = (st < nsteps) ? min(max(L - (t_step + 16 * mt), 0), 16) : 0;
+        return pd;
+    };
+    auto fire = [&](const Pending& pd, uint8_t* stg) __attribute__((always_inline)) {
+        __amdgpu_buffer_rsrc_t rs[4];  // per group: K tile 0, K tile 1, V tile 0, V tile 1
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            if (!(tile_mask & (1 << mt))) continue;
-            const int32_t n = (st < nsteps) ? min(max(L - (t_step + 16 * mt), 0), 16) : 0;
+            // every value of a buffer descriptor must be wave-uniform (SGPRs)
+            const int32_t n = __builtin_amdgcn_readfirstlane(pd.n[mt]);
+            uint64_t off = 0;
+            uint32_t rec = 0;
             if (n > 0) {
-                const int64_t o = tile_off[2 * st + mt];
-                const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)o);
-                const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)o >> 32));
-                off[mt] = ((uint64_t)hi << 32) | lo;
-                rec[mt] = (uint32_t)n * (uint32_t)a.token_stride;
+                off = ((uint64_t)__builtin_amdgcn_readfirstlane(pd.off_hi[mt]) << 32) |
+                      __builtin_amdgcn_readfirstlane(pd.off_lo[mt]);
+                rec = (uint32_t)n * (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a.token_stride);
             }
+            rs[mt] = tile_rsrc(a.kpool + off, rec);
+            rs[2 + mt] = tile_rsrc(a.vpool + off, rec);
         }
-        uint8_t* dst = stg + tl * C::STEP_BYTES + 1024 * rg * NW;
+        uint8_t* dst = stg + tl * C::STEP_BYTES;
 #pragma unroll
         for (int jj = 0; jj < NW; ++jj) {
-            const int mt = ld_tile[jj];
-            const uint8_t* pool = ld_v[jj] ? a.vpool : a.kpool;
-            load_lds16(tile_rsrc(pool + off[mt], rec[mt]), dst + 1024 * jj, voff[jj]);
+            __amdgpu_buffer_rsrc_t r;
+            if constexpr (BY_GROUP) {
+                r = rs[jj / PG];
+            } else {
+                const int gi = ld_group[jj];
+                r = gi == 0 ? rs[0] : (gi == 1 ? rs[1] : (gi == 2 ? rs[2] : rs[3]));
+            }
+            load_lds16(r, dst + ld_dst[jj], voff[jj]);
         }
     };
 
-    // ---- one 32-token step from stage sbase; edge steps hold masked (row, token) pairs ----
-    auto step = [&](int32_t t_step, const uint8_t* sbase, bool edge) __attribute__((always_inline)) {
-        // S^T = K * Q^T. The K reads of chunk j + 1 are issued before chunk j
-        // is converted; the scheduling barriers keep the compiler from hoisting
-        // every read and conversion of the step at once (register pressure).
-        f32x4 s[2][RT];
+    // ---- the fold of one 32-token step, in pieces: QK^T (per 64-dim chunk of
+    // K), the online softmax, PV (per 4 head_dim tiles). With four or more
+    // stages the loop runs QK of the next step between the softmax and the PV
+    // pieces of the current one, so the matrix core has work while the
+    // softmax's dependent VALU chain runs. ----
+    struct Scores {
+        f32x4 v[2][RT];  // S^T tiles: 16 tokens (mt) x 16 rows (nt)
+    };
+    auto qk_zero = [&](Scores& sc) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < RT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto kread = [&](int mt, int j) __attribute__((always_inline)) {
-            return *reinterpret_cast<const u32x4*>(sbase + kaddr + 1024 * (mt * KLOADS + j));
-        };
-        u32x4 kn0 = kread(0, 0), kn1 = kread(1, 0);
+            for (int nt = 0; nt < RT; ++nt) sc.v[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // K chunk j: bytes [64 j, 64 j + 64) of the 32 tokens (both 16-token
+    // tiles), the A operands of k-steps 2j and 2j+1
+    struct KChunk {
+        u32x4 w[2];
+    };
+    auto k_read = [&](const uint8_t* sbase, int j) __attribute__((always_inline)) -> KChunk {
+        KChunk kc;
 #pragma unroll
-        for (int j = 0; j < KLOADS; ++j) {
-            const u32x4 kw[2] = {kn0, kn1};
-            if (j + 1 < KLOADS) {
-                kn0 = kread(0, j + 1);
-                kn1 = kread(1, j + 1);
+        for (int mt = 0; mt < 2; ++mt)
+            kc.w[mt] = *reinterpret_cast<const u32x4*>(sbase + kaddr + 1024 * (mt * KLOADS + j));
+        return kc;
+    };
+    auto qk_fold = [&](const KChunk& kc, int j, Scores& sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const f16x8 k_lo = e4m3x8_to_f16x8(kc.w[mt].x, kc.w[mt].y);
+            const f16x8 k_hi = e4m3x8_to_f16x8(kc.w[mt].z, kc.w[mt].w);
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) {
+                sc.v[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, qop[nt][2 * j], sc.v[mt][nt], 0, 0, 0);
+                sc.v[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, qop[nt][2 * j + 1], sc.v[mt][nt], 0, 0, 0);
             }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const f16x8 k_lo = e4m3x8_to_f16x8(kw[mt].x, kw[mt].y);
-                const f16x8 k_hi = e4m3x8_to_f16x8(kw[mt].z, kw[mt].w);
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt) {
-                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, qop[nt][2 * j], s[mt][nt], 0, 0, 0);
-                    s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, qop[nt][2 * j + 1], s[mt][nt], 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
-
-        // online softmax, log2 domain, lazy reference maximum. Scores are scaled
-        // before masking, so a masked score is exactly -inf for any finite K scale.
+    };
+    auto qk_chunk = [&](const uint8_t* sbase, int j, Scores& sc) __attribute__((always_inline)) {
+        qk_fold(k_read(sbase, j), j, sc);
+    };
+    // online softmax, log2 domain, lazy reference maximum. Scores are scaled
+    // before masking, so a masked score is exactly -inf for any finite K scale.
+    auto softmax = [&](int32_t t_step, const Scores& sc, bool edge, f16x8 (&pop)[RT]) __attribute__((always_inline)) {
         float xs[RT][8];
         float smax[RT];
         bool need = false;
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xs[nt][e] = s[e >> 2][nt][e & 3] * cscale;
+            for (int e = 0; e < 8; ++e) xs[nt][e] = sc.v[e >> 2][nt][e & 3] * cscale;
         if (edge) {  // uniform: only steps that cross some row's causal limit or the live length
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
@@ -477,7 +520,6 @@ pfs_split_kernel(const SplitArgs a) {
         }
         // P = exp2(x - m_ref + kPBias); masked terms are exp2(-inf) = 0 (nb is
         // finite: it only changes together with a finite m_ref)
-        f16x8 pop[RT];
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
             f16x2 pp[4];
@@ -490,24 +532,34 @@ pfs_split_kernel(const SplitArgs a) {
             pop[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
                                              bit_cast_<uint32_t>(pp[2]), bit_cast_<uint32_t>(pp[3])});
         }
-
-        // O^T += V^T * P^T (V^T read transposed from LDS, two tiles ahead), l += 1 * P^T
-        auto vread = [&](int md) __attribute__((always_inline)) {
-            return lds_read_tr8(sbase + vaddr[md % SWB] + 16 * SWB * (md / SWB));
-        };
-        i32x2 vn[2];
-        vn[0] = vread(0);
-        if (MD > 1) vn[1] = vread(1);
+    };
+    // O^T += V^T * P^T for head_dim tiles [md0, md0 + 4), V^T read transposed from LDS
+    struct VChunk {
+        i32x2 w[4];
+    };
+    auto v_read = [&](const uint8_t* sbase, int md0) __attribute__((always_inline)) -> VChunk {
+        VChunk vc;
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-            const i32x2 w = vn[md & 1];
-            if (md + 2 < MD) vn[md & 1] = vread(md + 2);
-            const f16x8 vop = e4m3x8_to_f16x8((uint32_t)w.x, (uint32_t)w.y);
+        for (int u = 0; u < 4; ++u) {
+            const int md = md0 + u;
+            vc.w[u] = lds_read_tr8(sbase + vaddr[md % SWB] + 16 * SWB * (md / SWB));
+        }
+        return vc;
+    };
+    auto pv_fold = [&](const VChunk& vc, int md0, const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f16x8 vop = e4m3x8_to_f16x8((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
-                acc[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md][nt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md0 + u][nt], 0, 0, 0);
         }
+    };
+    auto pv_chunk = [&](const uint8_t* sbase, int md0, const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
+        pv_fold(v_read(sbase, md0), md0, pop);
+    };
+    // l += 1 * P^T (row sums from the same FP16 P)
+    auto row_sums = [&](const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt)
             lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
@@ -515,23 +567,95 @@ pfs_split_kernel(const SplitArgs a) {
 
     __syncthreads();  // tile table ready
 
-    // ---- pipeline: NS - 1 stages in flight ahead of the one being folded ----
-    static_for<NS - 1>([&](auto kc) __attribute__((always_inline)) { issue(decltype(kc)::value, stage(kc)); });
-    for (int32_t ss0 = 0; ss0 < nstages; ss0 += NS) {
-        static_for<NS>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            const int32_t ss = ss0 + k;
-            // this wave's loads of stage ss are done once at most (NS - 2) * NW
-            // younger ones are in flight; the barrier makes every wave's loads of
-            // stage ss visible and retires every read of the stage refilled next
-            wait_vm_and_barrier<(NS - 2) * NW>();
-            issue(ss + NS - 1, stage(std::integral_constant<int, (k + NS - 1) % NS>{}));
-            const int32_t st = ss * TP + tl;
-            if (ss < nstages && st < nsteps) {
-                const int32_t t_step = tok0 + st * kStep;
-                step(t_step, stage(kc), t_step + kStep > lim_lo);
-            }
-        });
+    constexpr bool PIPE = NS >= 4;
+    static_for<NS - 1>([&](auto kc) __attribute__((always_inline)) { fire(prep(decltype(kc)::value), stage(kc)); });
+    Pending pend = prep(NS - 1);  // loads of the next stage to issue
+    if constexpr (PIPE) {
+        // ---- NS - 2 stages in flight ahead of the one whose QK is folded ----
+        Scores sc_cur;
+        f16x8 pop[RT];
+        wait_vm_and_barrier<(NS - 2) * NW>();  // stage 0 ready
+        qk_zero(sc_cur);
+#pragma unroll
+        for (int j = 0; j < KLOADS; ++j) {
+            qk_chunk(stage(std::integral_constant<int, 0>{}), j, sc_cur);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int32_t ss0 = 0; ss0 < nstages; ss0 += NS) {
+            static_for<NS>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                const int32_t ss = ss0 + k;
+                // stage ss + 1 is complete once at most (NS - 3) * NW of this
+                // wave's loads are younger; past the barrier every wave is done
+                // with stage ss - 1, which the issue refills
+                wait_vm_and_barrier<(NS - 3) * NW>();
+                fire(pend, stage(std::integral_constant<int, (k + NS - 1) % NS>{}));
+                pend = prep(ss + NS);
+                const int32_t st = ss * TP + tl;
+                if (ss < nstages && st < nsteps) {
+                    const int32_t t_step = tok0 + st * kStep;
+                    const uint8_t* sb = stage(kc);
+                    const uint8_t* sb_next = stage(std::integral_constant<int, (k + 1) % NS>{});
+                    Scores sc_next;  // QK of this wave's next step (stage ss + 1; zeros or unused past the end)
+                    // after the softmax, group c folds K chunk c of the next step
+                    // and V tiles [4c, 4c + 4) of this one; the LDS reads of
+                    // group c + 1 are issued before group c computes
+                    KChunk k_nxt = k_read(sb_next, 0), k_cur;
+                    VChunk v_nxt = v_read(sb, 0), v_cur;
+                    softmax(t_step, sc_cur, t_step + kStep > lim_lo, pop);
+                    qk_zero(sc_next);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int c = 0; c < KLOADS; ++c) {
+                        k_cur = k_nxt;
+                        v_cur = v_nxt;
+                        if (c + 1 < KLOADS) {
+                            k_nxt = k_read(sb_next, c + 1);
+                            v_nxt = v_read(sb, 4 * (c + 1));
+                        }
+                        qk_fold(k_cur, c, sc_next);
+                        pv_fold(v_cur, 4 * c, pop);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    row_sums(pop);
+                    sc_cur = sc_next;
+                }
+            });
+        }
+    } else {
+        // ---- NS - 1 stages in flight ahead of the one being folded ----
+        for (int32_t ss0 = 0; ss0 < nstages; ss0 += NS) {
+            static_for<NS>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                const int32_t ss = ss0 + k;
+                // this wave's loads of stage ss are done once at most (NS - 2) * NW
+                // younger ones are in flight; the barrier makes every wave's loads of
+                // stage ss visible and retires every read of the stage refilled next
+                wait_vm_and_barrier<(NS - 2) * NW>();
+                fire(pend, stage(std::integral_constant<int, (k + NS - 1) % NS>{}));
+                pend = prep(ss + NS);
+                const int32_t st = ss * TP + tl;
+                if (ss < nstages && st < nsteps) {
+                    const int32_t t_step = tok0 + st * kStep;
+                    const uint8_t* sb = stage(kc);
+                    Scores sc;
+                    f16x8 pop[RT];
+                    qk_zero(sc);
+#pragma unroll
+                    for (int j = 0; j < KLOADS; ++j) {
+                        qk_chunk(sb, j, sc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    softmax(t_step, sc, t_step + kStep > lim_lo, pop);
+#pragma unroll
+                    for (int c = 0; c < KLOADS; ++c) {
+                        pv_chunk(sb, 4 * c, pop);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    row_sums(pop);
+                }
+            });
+        }
     }
     wait_vm_and_barrier<0>();  // no load into LDS is still in flight
 
@@ -632,35 +756,41 @@ struct CombineArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// One workgroup of 16 waves per output row (request, KV head, row). Wave w
-// sums the w-th contiguous run of the visible splits in ascending split order
-// (its loads are independent, so a wave keeps its whole run in flight); the 16
-// runs are then added in wave order. The global max is a plain max (exact, so
-// any order). Each lane owns head_dim/64 columns.
-constexpr int kCombineWaves = 16;
+// One workgroup of 256 threads per (request, KV head, row, 64-column slice),
+// so that even one request's few rows spread over every CU. Thread t owns the
+// 4 columns 4 (t % 16) .. of the slice and the visible splits s with
+// s % 16 == t / 16 (its split lane), folded in ascending order CH at a time
+// (their loads are issued together) against a running maximum; the 16 split
+// lanes of each column group are then merged in lane order against the
+// global maximum.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineSplitLanes = 16;
+constexpr int kCombineChunk = 8;
 
 template <int D>
-__global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const CombineArgs a) {
-    constexpr int CPL = D / 64;  // columns per lane
-    __shared__ float red[kCombineWaves];
-    __shared__ float part_l[kCombineWaves];
-    __shared__ float part_acc[kCombineWaves][D];
+__global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const CombineArgs a) {
+    constexpr int SL = kCombineSplitLanes, CH = kCombineChunk, SLICES = D / 64;
+    __shared__ float part_m[SL][16];
+    __shared__ float part_l[SL][16];
+    __shared__ f32x4 part_acc[SL][16];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = blockIdx.x;
+    const int t = threadIdx.x;
+    const int cg = t % 16;  // column group of the slice
+    const int sl = t / 16;  // split lane
+    const int r = blockIdx.x / SLICES;
+    const int col0 = (blockIdx.x % SLICES) * 64 + 4 * cg;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
     const int i = r / a.group;
     const int h = a.qhead[g * a.group + (r % a.group)];
-    _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D;
+    _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + col0;
 
     const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
     const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
     if (n == 0) {  // nothing visible: defined output +0.0
-        if (wave == 0) {
+        if (sl == 0) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) dst[lane * CPL + c] = (_Float16)0.0f;
+            for (int c = 0; c < 4; ++c) dst[c] = (_Float16)0.0f;
         }
         return;
     }
@@ -669,58 +799,58 @@ __global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const C
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
     const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
 
-    float mx = -INFINITY;
-    for (int s = threadIdx.x; s < ns; s += 64 * kCombineWaves) mx = fmaxf(mx, ml[slot0 + s * stride].x);
-    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    mx = max_over_lane_groups(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    float M = red[0];
+    float M = -INFINITY, lw = 0.0f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = sl; c0 < ns; c0 += SL * CH) {
+        float2 v[CH];
+        f32x4 x[CH];
 #pragma unroll
-    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red[w]);
-
-    const int per = (ns + kCombineWaves - 1) / kCombineWaves;
-    const int s0 = wave * per;
-    const int s1 = min(ns, s0 + per);
-    float lw = 0.0f;
-    float acc[CPL];
+        for (int u = 0; u < CH; ++u) {
+            const int sp = c0 + u * SL;
+            if (sp < ns) {
+                const int64_t slot = slot0 + sp * stride;
+                v[u] = ml[slot];
+                x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + col0);
+            } else {
+                v[u] = make_float2(-INFINITY, 0.0f);
+                x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float cm = M;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
-    for (int s = s0; s < s1; ++s) {
-        const int64_t slot = slot0 + s * stride;
-        const float2 v = ml[slot];
-        const float f = (v.x == M) ? 1.0f : __builtin_amdgcn_exp2f(v.x - M);
-        lw += f * v.y;
-        const float* src = a.ws_acc + slot * D + lane * CPL;
-        if constexpr (CPL == 4) {
-            const f32x4 xx = *reinterpret_cast<const f32x4*>(src);
+        for (int u = 0; u < CH; ++u) cm = fmaxf(cm, v[u].x);
+        if (cm != M) {  // a larger maximum: rescale the running state (empty state: factor 0)
+            const float al = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
+            lw *= al;
+            acc *= al;
+            M = cm;
+        }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] += f * xx[c];
-        } else if constexpr (CPL == 2) {
-            const float2 xx = *reinterpret_cast<const float2*>(src);
-            acc[0] += f * xx.x;
-            acc[1] += f * xx.y;
-        } else {
-            acc[0] += f * src[0];
+        for (int u = 0; u < CH; ++u) {
+            const float f = (v[u].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[u].x - M);
+            lw += f * v[u].y;
+            acc += f * x[u];
         }
     }
-    if (lane == 0) part_l[wave] = lw;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) part_acc[wave][lane * CPL + c] = acc[c];
+    part_m[sl][cg] = M;
+    part_l[sl][cg] = lw;
+    part_acc[sl][cg] = acc;
     __syncthreads();
-    if (wave != 0) return;
-    float lt = part_l[0];
+    if (sl != 0) return;
+    float Mg = part_m[0][cg];
 #pragma unroll
-    for (int w = 1; w < kCombineWaves; ++w) lt += part_l[w];
+    for (int k = 1; k < SL; ++k) Mg = fmaxf(Mg, part_m[k][cg]);
+    float lt = 0.0f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+        const float fw = (part_m[k][cg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(part_m[k][cg] - Mg);
+        lt += fw * part_l[k][cg];
+        num += fw * part_acc[k][cg];
+    }
     const float vs = a.vscale[g];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int d = lane * CPL + c;
-        float num = part_acc[0][d];
-#pragma unroll
-        for (int w = 1; w < kCombineWaves; ++w) num += part_acc[w][d];
-        dst[d] = (_Float16)((num * vs) / lt);
-    }
+    for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((num[c] * vs) / lt);
 }
 
 // Paged E4M3 -> dense FP16: one thread per 16 bytes of one (token, KV head).
@@ -852,11 +982,11 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.tokens_per_split = plan->tokens_per_split;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid(plan->rows, p.num_kv_heads, p.batch);
+    const dim3 grid(plan->rows * (p.head_dim / 64), p.num_kv_heads, p.batch);
     switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
-        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
-        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, dim3(64 * kCombineWaves), 0, s, ca); break;
+        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, dim3(kCombineThreads), 0, s, ca); break;
+        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, dim3(kCombineThreads), 0, s, ca); break;
+        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, dim3(kCombineThreads), 0, s, ca); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
