@@ -316,7 +316,14 @@ pfs_split_kernel(const SplitArgs a) {
         lim[nt] = (r < a.rows) ? clamp_i((int64_t)L - a.q + r / a.group + 1, 0, L) : L;
     }
     const int32_t lim_lo = clamp_i((int64_t)L - a.q + 1, 0, L);  // smallest limit of any real row
-    const float cscale = a.sm_scale_log2e * a.kscale[g];  // score scale, log2 domain
+    float cscale = a.sm_scale_log2e * a.kscale[g];  // score scale, log2 domain
+    if (cscale < 0.0f) {  // keep the scale non-negative: max(s) * c is then the max of the scaled scores
+        cscale = -cscale;
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) qop[nt][ks] = -qop[nt][ks];
+    }
 
     f32x4 acc[MD][RT];
     f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
@@ -489,19 +496,22 @@ pfs_split_kernel(const SplitArgs a) {
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xs[nt][e] = sc.v[e >> 2][nt][e & 3] * cscale;
+            for (int e = 0; e < 8; ++e) xs[nt][e] = sc.v[e >> 2][nt][e & 3];
         if (edge) {  // uniform: only steps that cross some row's causal limit or the live length
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < 8; ++e) {
+                    xs[nt][e] *= cscale;
                     if (t_step + (e >> 2) * 16 + 4 * lg + (e & 3) >= lim[nt]) xs[nt][e] = -INFINITY;
+                }
         }
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
             const float mx = fmaxf(fmaxf(fmaxf(xs[nt][0], xs[nt][1]), fmaxf(xs[nt][2], xs[nt][3])),
                                    fmaxf(fmaxf(xs[nt][4], xs[nt][5]), fmaxf(xs[nt][6], xs[nt][7])));
             smax[nt] = max_over_lane_groups(mx);
+            if (!edge) smax[nt] *= cscale;
             need |= (smax[nt] > mref[nt] + kTau);
         }
         if (__builtin_expect(__any(need), 0)) {
@@ -525,8 +535,9 @@ pfs_split_kernel(const SplitArgs a) {
             f16x2 pp[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(xs[nt][e] + nb[nt]);
-                const float p1 = __builtin_amdgcn_exp2f(xs[nt][e + 1] + nb[nt]);
+                const float c = edge ? 1.0f : cscale;
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e], c, nb[nt]));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e + 1], c, nb[nt]));
                 pp[e >> 1] = f16x2{(_Float16)p0, (_Float16)p1};
             }
             pop[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),

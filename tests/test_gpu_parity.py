@@ -96,6 +96,21 @@ def test_rows_without_visible_keys_are_positive_zero():
     judge(out, oracle_ref(w), "zero rows")
 
 
+def test_negative_and_zero_scales():
+    """k_scale and v_scale are plain FP32 factors: a negative K scale flips the
+    scores, a zero K scale makes every visible key equally likely, a negative V
+    scale flips the output. The oracle applies them exactly."""
+    w = W.build(seed=47, batch=2, q=8, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=32,
+                lengths=[700, 260])
+    # the workload's own magnitudes (absmax / 448 per head), with signs flipped and one K scale zeroed
+    w.k_scale = (w.k_scale * np.array([-1.0, 0.0, 1.0, -1.0])).astype(np.float32)
+    w.v_scale = (w.v_scale * np.array([1.0, -1.0, 1.0, -1.0])).astype(np.float32)
+    log(f"[scales] k={w.k_scale.tolist()} v={w.v_scale.tolist()}")
+    for tps in (0, 128):
+        out = to_np(run(w, tokens_per_split=tps)[0])
+        judge(out, oracle_ref(w), f"signed scales tps={tps}")
+
+
 def test_padded_strides_match_contiguous_bitwise():
     kw = dict(batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64, lengths=[1500, 400])
     a = W.build(seed=41, **kw)
