@@ -41,8 +41,15 @@ def note(msg: str) -> None:
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with comments and blank lines removed,
+    so that profiles stay valid across comment-only edits."""
+    import re
+
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles(cfg: int):

@@ -6,8 +6,8 @@
 //   pfs_split_kernel      per-split QK^T (MFMA), online softmax, PV (MFMA);
 //                         emits FP32 (max, sum, unnormalized PV) per split
 //   pfs_combine_kernel    rescales the splits, sums them in a fixed order
-//                         (ascending runs, runs in order), normalizes and
-//                         rounds once to FP16
+//                         (ascending within a split lane, lanes in order),
+//                         normalizes and rounds once to FP16
 //
 // The method ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32
 // partials", final status, revision 3 bullet; "[Kernel] Finalize the audited
@@ -17,36 +17,42 @@
 // scalar/tensor-core kernel; here it is built around CDNA4's 64-wide
 // wavefronts and v_mfma_f32_16x16x32_f16.
 //
-// Work decomposition of the split kernel (one workgroup = 4 waves per split,
-// KV head and row block):
-//  * rows: up to 64 of the R = G*q query rows of one KV head per workgroup
-//    (row r = i*G + jj: draft row i, jj-th query head of the group), padded to
-//    16-row MFMA tiles; more rows become row blocks of the grid. The FP32
-//    accumulators of every row and every head_dim column stay in registers.
-//  * tokens: wave w takes partitions w, w+4, w+8, ... of the split, in
-//    ascending order; the four wave states are merged in wave order at the end.
+// Work decomposition of the split kernel (one workgroup per split, KV head and
+// row block; W = RG * TP waves):
+//  * rows: the R = G*q query rows of one KV head (row r = i*G + jj: draft row
+//    i, jj-th query head of the group), padded to 16-row MFMA tiles. RG row
+//    groups of RT tiles each; rows beyond RG*RT tiles become row blocks of the
+//    grid. A wave's FP32 accumulators (its rows x every head_dim column) and
+//    its Q^T operands stay in registers.
+//  * tokens: TP token lanes; lane tl folds the 32-token steps tl, tl+TP, ... of
+//    the split in ascending order. The lanes of a row group are merged in a
+//    fixed tree order at the end.
+//  * K/V bytes go from HBM straight into LDS stages (buffer_load_dwordx4 ...
+//    lds) that all waves share: a stage holds TP steps, stages are issued
+//    ahead and every stage costs one barrier. Each stage is its own LDS object
+//    so that the compiler waits only for the loads into the stage it reads.
+//  * the byte offset of every 16-token tile of the split is computed once from
+//    the block table into an LDS table; each tile's buffer descriptor ends at
+//    the live length, so bytes beyond it arrive as zeros.
 //  * scores are computed transposed, S^T = K * Q^T (A = K: 16 tokens x 32 dims,
 //    B = Q^T: 32 dims x 16 rows), so each lane ends up holding 4 consecutive
 //    tokens of one row: exactly the token slots the PV product
 //    O^T = V^T * P^T needs in its B operand. P never leaves registers.
-//  * K goes from HBM straight into MFMA A operands: lane (c, g) of a 16-token
-//    tile loads 16-byte chunks of token c, so each load instruction reads 64
-//    contiguous bytes of 16 tokens; the E4M3 bytes are converted in registers.
-//  * V^T needs 8 tokens of one head_dim column per lane: V rows are loaded
-//    with 16-byte loads (4 whole token rows per instruction), written to the
-//    wave's LDS stage with an XOR swizzle of the 16-byte chunks, and read back
-//    transposed with ds_read_b64_tr_b8: in each 16-lane block, lane j names
-//    8 bytes of one token row and every lane receives one column of 8 tokens.
-//  * Q^T operands are staged once per workgroup in LDS in the exact per-lane
-//    order the MFMA B operand needs (one ds_read_b128 per operand).
+//  * K sits in LDS where each lane reads its own MFMA A operand (16 bytes of
+//    one token); V rows sit with an XOR swizzle of 16-byte chunks and are read
+//    transposed with ds_read_b64_tr_b8: in each 16-lane block, lane j names 8
+//    bytes of one token row and every lane receives one column of 8 tokens.
+//  * with four or more stages a wave folds the QK of its next step together
+//    with the PV of its current one.
 //
 // Numerics: FP16 MFMA operands with FP32 accumulation; the per-head K scale,
-// the softmax scale and log2(e) are applied to FP32 scores; probabilities are
-// exp2(s - m_ref + 7) rounded once to FP16 against a lazily raised reference
-// maximum m_ref; the row sums come from the matrix core (a ones row times the
-// same FP16 P the PV product uses); V's scale is applied once in the combine.
-// Masked scores are selected to -inf and K/V bytes beyond the live length are
-// never loaded (zero), so NaN tail bytes cannot leak.
+// the softmax scale and log2(e) are applied to FP32 scores (inside the exp2
+// argument); probabilities are exp2(s - m_ref + 7) rounded once to FP16
+// against a lazily raised reference maximum m_ref; the row sums come from the
+// matrix core (a ones row times the same FP16 P the PV product uses); V's
+// scale is applied once in the combine. Masked scores are selected to -inf and
+// K/V bytes beyond the live length are never loaded (zero), so NaN tail bytes
+// cannot leak.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
