@@ -71,8 +71,11 @@ typedef struct ihipStream_t* pfs_stream_t;
  * for page in [0, num_pool_pages), slot in [0, page_size), d in [0, head_dim)
  * (the pages' [num_blocks, block_size, kv_heads, head_dim] uint8 layout with
  * byte strides; "... FP32 partials", AI integration review). The head_dim
- * bytes of one (page, slot, kv_head) are contiguous. K and V pools share the
- * same strides.
+ * bytes of one (page, slot, kv_head) are contiguous. The rows of a page must
+ * not overlap: either the token stride holds all heads of a token
+ * ([page][slot][head][d], token-major) or the head stride holds all slots of a
+ * head ([page][head][slot][d], head-major). K and V pools share the same
+ * strides.
  *
  * Q and out: contiguous [batch, q, num_q_heads, head_dim] FP16.
  */

@@ -89,10 +89,18 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
     if (!is_multiple(p.kv_head_stride, 16) || !is_multiple(p.kv_token_stride, 16) ||
         !is_multiple(p.kv_page_stride, 16))
         return PFS_ERR_ALIGNMENT;
+    // The (slot, KV head) rows of a page must not overlap: either a token's
+    // heads nest inside the token stride ([page][slot][head][d]) or a head's
+    // tokens nest inside the head stride ([page][head][slot][d]).
+    if (p.kv_head_stride < p.head_dim || p.kv_token_stride < p.head_dim) return PFS_ERR_SHAPE;
     const int64_t head_span = (int64_t)(p.num_kv_heads - 1) * p.kv_head_stride + p.head_dim;
-    if (p.kv_head_stride < p.head_dim) return PFS_ERR_SHAPE;
-    if (p.kv_token_stride < head_span) return PFS_ERR_SHAPE;
-    if (p.kv_page_stride < (int64_t)(p.page_size - 1) * p.kv_token_stride + head_span) return PFS_ERR_SHAPE;
+    const int64_t token_span = (int64_t)(p.page_size - 1) * p.kv_token_stride + p.head_dim;
+    const bool token_major = p.kv_token_stride >= head_span;
+    const bool head_major = p.kv_head_stride >= token_span;
+    if (!token_major && !head_major) return PFS_ERR_SHAPE;
+    const int64_t page_span = token_major ? (int64_t)(p.page_size - 1) * p.kv_token_stride + head_span
+                                          : (int64_t)(p.num_kv_heads - 1) * p.kv_head_stride + token_span;
+    if (p.kv_page_stride < page_span) return PFS_ERR_SHAPE;
     if ((double)p.kv_page_stride * (double)p.num_pool_pages > 4.0e18) return PFS_ERR_SHAPE;
 
     // head map: in range and uniform groups

@@ -101,6 +101,17 @@ def test_invalid_problems_are_rejected(over, status):
     assert plan_status(**over) == _lib.STATUS_CODE[status]
 
 
+def test_head_major_pool_layout_is_accepted():
+    # [page][head][slot][d]: 2 heads x 64 slots x 256 bytes per page
+    assert plan_status(kv_token_stride=256, kv_head_stride=64 * 256, kv_page_stride=2 * 64 * 256) == 0
+    # the head stride must hold a head's 64 slots
+    assert plan_status(kv_token_stride=256, kv_head_stride=63 * 256,
+                       kv_page_stride=4 * 64 * 256) == _lib.STATUS_CODE["PFS_ERR_SHAPE"]
+    # and the page stride both heads
+    assert plan_status(kv_token_stride=256, kv_head_stride=64 * 256,
+                       kv_page_stride=2 * 64 * 256 - 16) == _lib.STATUS_CODE["PFS_ERR_SHAPE"]
+
+
 def test_pages_stride_counterexample_is_rejected():
     g = json.load(open(os.path.join(GOLDEN, "stride_counterexample.json")))
     pages, page, heads, dim = g["shape"]

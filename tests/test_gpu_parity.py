@@ -96,6 +96,22 @@ def test_rows_without_visible_keys_are_positive_zero():
     judge(out, oracle_ref(w), "zero rows")
 
 
+def test_head_major_pool_matches_token_major_bitwise():
+    """The same bytes laid out [page][head][slot][d] (strides from the tensor
+    view) give the bit-identical output of the [page][slot][head][d] layout."""
+    w = W.build(seed=43, batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                lengths=[3000, 700])
+    y, t = run(w)
+    ya = to_np(y)
+    judge(ya, oracle_ref(w), "token-major")
+    kh = t["k_pool"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vh = t["v_pool"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    log(f"[layout] head-major strides {tuple(kh.stride())}")
+    yh = to_np(pfs.verify(t["q"], kh, vh, t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
+                          head_map=t["head_map"], sm_scale=t["sm_scale"]))
+    assert np.array_equal(ya.view(np.uint16), yh.view(np.uint16))
+
+
 def test_negative_and_zero_scales():
     """k_scale and v_scale are plain FP32 factors: a negative K scale flips the
     scores, a zero K scale makes every visible key equally likely, a negative V
