@@ -64,6 +64,12 @@ def _load():
     lib.oracle_max_threads.argtypes = []
     lib.oracle_verify.restype = c.c_int
     lib.oracle_verify.argtypes = [c.c_int32] * 9 + [c.c_int64] * 3 + [P] * 9 + [c.c_double, P, c.c_int32]
+    lib.oracle_e4m3_encode.restype = c.c_uint32
+    lib.oracle_e4m3_encode.argtypes = [c.c_float]
+    lib.oracle_quantize_fp16.restype = c.c_uint32
+    lib.oracle_quantize_fp16.argtypes = [c.c_uint32, c.c_float]
+    lib.oracle_kv_append.restype = c.c_int
+    lib.oracle_kv_append.argtypes = [c.c_int32] * 7 + [c.c_int64] * 3 + [P] * 8
     _lib = lib
     return lib
 
@@ -122,3 +128,40 @@ def verify(w, *, partition_tokens: Optional[int] = None, unit_mask: Optional[np.
     if rc != 0:
         raise RuntimeError(f"oracle_verify failed with code {rc}")
     return out
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """E4M3FN code (uint8) of each FP32 value: nearest, ties to even,
+    saturating at +-448, NaN -> 0x7F."""
+    lib = _load()
+    v = np.asarray(values, dtype=np.float32).ravel()
+    return np.array([lib.oracle_e4m3_encode(float(x)) for x in v], dtype=np.uint8).reshape(np.shape(values))
+
+
+def quantize_fp16(bits, scale: float) -> np.ndarray:
+    """E4M3 code of (float)x / scale for FP16 bit patterns ``bits``."""
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    s = float(np.float32(scale))
+    return np.array([lib.oracle_quantize_fp16(int(x), s) for x in b], dtype=np.uint8).reshape(np.shape(bits))
+
+
+def kv_append(w, k_new_fp16: np.ndarray, v_new_fp16: np.ndarray, k_scale=None, v_scale=None):
+    """Store the draft tokens' FP16 K/V [B, q, Hkv, D] of workload ``w`` into
+    copies of its pools; returns (k_pool, v_pool) as new uint8 arrays."""
+    kp = np.array(w.k_pool, dtype=np.uint8, copy=True)
+    vp = np.array(w.v_pool, dtype=np.uint8, copy=True)
+    kn = np.ascontiguousarray(k_new_fp16, dtype=np.float16).view(np.uint16)
+    vn = np.ascontiguousarray(v_new_fp16, dtype=np.float16).view(np.uint16)
+    assert kn.shape == (w.batch, w.q, w.num_kv_heads, w.head_dim) and vn.shape == kn.shape
+    ks = np.ascontiguousarray(w.k_scale if k_scale is None else k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(w.v_scale if v_scale is None else v_scale, dtype=np.float32)
+    bt = np.ascontiguousarray(w.block_table, dtype=np.int32)
+    ll = np.ascontiguousarray(w.live_len, dtype=np.int32)
+    rc = _load().oracle_kv_append(
+        w.batch, w.q, w.num_kv_heads, w.head_dim, w.page_size, w.max_pages_per_row, w.num_pool_pages,
+        w.page_stride, w.token_stride, w.head_stride, _ptr(kn), _ptr(vn), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(ll),
+        _ptr(kp), _ptr(vp))
+    if rc != 0:
+        raise RuntimeError(f"oracle_kv_append failed with code {rc}")
+    return kp, vp

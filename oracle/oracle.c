@@ -294,3 +294,83 @@ int32_t oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/*
+ * Quantize-on-write: the K/V of a request's q draft tokens, FP16, stored into
+ * its paged E4M3 pool with the per-KV-head scale (the step before verify;
+ * "[Kernel] Preserve DFlash2 sampling precision ...", Purpose: deferred
+ * accepted-slot writes; "[Bugfix] Use FP32 state ...", Test Plan: KV scaling).
+ *
+ * Readings (listed in the design doc): the stored byte is the E4M3FN code nearest
+ * to the FP32 quotient x / scale (IEEE single division, correctly rounded),
+ * ties to the even code, saturating at +-448 (infinities too); a NaN quotient
+ * stores 0x7F. Draft row i of request b lands at token L_b - q + i; rows that
+ * would land before token 0 (L_b < q) are not written.
+ */
+
+/* E4M3FN code nearest to the FP32 value v, ties to even, saturating. */
+uint32_t oracle_e4m3_encode(float v) {
+    if (isnan(v)) return 0x7Fu;
+    const uint32_t sign = signbit(v) ? 0x80u : 0u;
+    const double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7Eu;  /* 448 = S.1111.110 */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid: multiples of 2^-9; rounding to 8 gives the smallest normal */
+        const double n = nearbyint(a * 512.0);
+        return sign | (uint32_t)n;
+    }
+    int e = (int)floor(log2(a));
+    /* guard against log2 rounding at exact powers of two */
+    if (ldexp(1.0, e) > a) e -= 1;
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    double sig = nearbyint(a / ldexp(1.0, e - 3)); /* 8 .. 16 */
+    if (sig >= 16.0) {
+        sig = 8.0;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && sig > 14.0)) return sign | 0x7Eu;
+    return sign | (uint32_t)(((e + 7) << 3) | ((int)sig - 8));
+}
+
+/* FP16 bits x stored with scale s: the code of (float)x / s. */
+uint32_t oracle_quantize_fp16(uint32_t bits, float scale) {
+    const float x = (float)oracle_fp16_value(bits);
+    const float quotient = x / scale;
+    return oracle_e4m3_encode(quotient);
+}
+
+/*
+ * Write the draft tokens' K and V into the pools (in place).
+ *   k_new/v_new [batch, q, num_kv_heads, head_dim] IEEE half bit patterns
+ *   pools, strides, block_table, live_len as for oracle_verify; lengths are
+ *   clamped into [0, max_pages_per_row * page_size].
+ * Returns ORACLE_OK, or ORACLE_ERR_ARG for a block-table entry outside the pool.
+ */
+int oracle_kv_append(int32_t batch, int32_t q, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t max_pages_per_row, int32_t num_pool_pages, int64_t page_stride,
+                     int64_t token_stride, int64_t head_stride, const uint16_t* k_new, const uint16_t* v_new,
+                     const float* k_scale, const float* v_scale, const int32_t* block_table,
+                     const int32_t* live_len, uint8_t* k_pool, uint8_t* v_pool) {
+    const int64_t capacity = (int64_t)max_pages_per_row * page_size;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = live_len[b];
+        if (L < 0) L = 0;
+        if (L > capacity) L = capacity;
+        for (int32_t i = 0; i < q; ++i) {
+            const int64_t t = L - q + i;
+            if (t < 0) continue;
+            const int32_t page = block_table[(int64_t)b * max_pages_per_row + t / page_size];
+            if (page < 0 || page >= num_pool_pages) return ORACLE_ERR_ARG;
+            const int64_t base = (int64_t)page * page_stride + (t % page_size) * token_stride;
+            for (int32_t g = 0; g < num_kv_heads; ++g) {
+                const int64_t src = (((int64_t)b * q + i) * num_kv_heads + g) * head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) {
+                    const int64_t dst = base + (int64_t)g * head_stride + d;
+                    k_pool[dst] = (uint8_t)oracle_quantize_fp16(k_new[src + d], k_scale[g]);
+                    v_pool[dst] = (uint8_t)oracle_quantize_fp16(v_new[src + d], v_scale[g]);
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}

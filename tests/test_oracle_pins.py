@@ -329,3 +329,88 @@ def test_midpoint_construction_discriminates():
             y16 = np.float32(o16.mean(dtype=np.float32)) * np.float32(2.0 ** -6)
             legacy_bad += int(np.float16(y16).view(np.uint16) != want)
     assert legacy_bad > 0
+
+
+# ---- quantize-on-write (the E4M3 encoder and the draft-token append) ----
+
+def _torch_e4m3_codes(v32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn conversion (round to nearest even) of
+    values already clamped to +-448 (torch returns NaN above 464)."""
+    t = torch.from_numpy(np.clip(v32.astype(np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    table = oracle.e4m3_table()
+    finite = [b for b in range(256) if not math.isnan(table[b])]
+    got = oracle.e4m3_encode(table[finite].astype(np.float32))
+    assert np.array_equal(got, np.array(finite, dtype=np.uint8))
+
+
+def test_e4m3_encode_matches_torch_and_brute_force_nearest():
+    rng = np.random.default_rng(5)
+    table = oracle.e4m3_table()
+    codes = np.array([b for b in range(256) if not math.isnan(table[b])])
+    vals = table[codes]
+    mids = ((vals[:, None] + vals[None, :]) / 2).ravel()  # every midpoint between two codes (and the codes)
+    x = np.concatenate([
+        rng.normal(0, 1, 4000), rng.normal(0, 100, 2000), rng.uniform(-2 ** -6, 2 ** -6, 2000),
+        mids[np.abs(mids) <= 448], [0.0, -0.0, 448.0, -448.0, 2 ** -10, -(2 ** -10), 3 * 2 ** -10],
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = oracle.e4m3_encode(x)
+    assert np.array_equal(got, _torch_e4m3_codes(x))
+    # brute force: nearest finite code by value, ties to the even code
+    for v, c in zip(x[:3000], got[:3000]):
+        d = np.abs(vals - float(v))
+        best = codes[d == d.min()]
+        best = best[best % 2 == 0] if len(best) > 1 else best
+        if float(v) == 0.0:
+            continue  # +-0 keep their sign (checked below)
+        assert c == best[0] or (table[c] == table[best[0]]), (v, c, best)
+    assert oracle.e4m3_encode(np.float32(-0.0)) == 0x80 and oracle.e4m3_encode(np.float32(0.0)) == 0x00
+
+
+def test_e4m3_encode_saturates_and_maps_nan():
+    big = np.array([448.0, 449.0, 463.99, 464.0, 480.0, 1.0e9, np.inf], dtype=np.float32)
+    assert np.all(oracle.e4m3_encode(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode(-big) == 0xFE)
+    assert oracle.e4m3_encode(np.float32(np.nan)) == 0x7F
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0027, 2.0 ** -6, 16.0, 3.0e-5])
+def test_quantize_fp16_is_the_code_of_the_fp32_quotient(scale):
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16).astype(np.float32)
+    keep = np.isfinite(x)
+    q32 = (x[keep] / np.float32(scale)).astype(np.float32)
+    got = oracle.quantize_fp16(bits[keep], scale)
+    big = np.abs(q32) > 448
+    assert np.all(got[big & (q32 > 0)] == 0x7E) and np.all(got[big & (q32 < 0)] == 0xFE)
+    assert np.array_equal(got[~big], _torch_e4m3_codes(q32[~big]))
+
+
+def test_kv_append_writes_exactly_the_draft_slots():
+    w = W.build(seed=61, batch=3, q=4, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                lengths=[37, 2, 0])
+    rng = np.random.default_rng(62)
+    kn = rng.normal(0, 3, (3, 4, 2, 64)).astype(np.float16)
+    vn = rng.normal(0, 3, (3, 4, 2, 64)).astype(np.float16)
+    kp, vp = oracle.kv_append(w, kn, vn)
+    view_k, view_v = w.pool_view(kp), w.pool_view(vp)
+    old_k = w.pool_view(np.asarray(w.k_pool))
+    touched = np.zeros(view_k.shape[:2], dtype=bool)
+    for b, L in enumerate(w.live_len):
+        for i in range(w.q):
+            t = int(L) - w.q + i
+            if t < 0:
+                continue
+            page, slot = w.block_table[b, t // 16], t % 16
+            touched[page, slot] = True
+            for g in range(2):
+                assert np.array_equal(view_k[page, slot, g], oracle.quantize_fp16(kn[b, i, g].view(np.uint16),
+                                                                                   w.k_scale[g]))
+                assert np.array_equal(view_v[page, slot, g], oracle.quantize_fp16(vn[b, i, g].view(np.uint16),
+                                                                                   w.v_scale[g]))
+    assert touched.sum() == 4 + 2  # request 1 (L=2 < q=4) writes only its last two rows; request 2 nothing
+    assert np.array_equal(view_k[~touched], old_k[~touched])
