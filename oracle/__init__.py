@@ -68,6 +68,10 @@ def _load():
     lib.oracle_e4m3_encode.argtypes = [c.c_float]
     lib.oracle_quantize_fp16.restype = c.c_uint32
     lib.oracle_quantize_fp16.argtypes = [c.c_uint32, c.c_float]
+    lib.oracle_fp16_rne.restype = c.c_uint32
+    lib.oracle_fp16_rne.argtypes = [c.c_double]
+    lib.oracle_dequant.restype = c.c_int
+    lib.oracle_dequant.argtypes = [c.c_int32] * 6 + [c.c_int64] * 3 + [P] * 5
     lib.oracle_kv_append.restype = c.c_int
     lib.oracle_kv_append.argtypes = [c.c_int32] * 7 + [c.c_int64] * 3 + [P] * 8
     _lib = lib
@@ -165,3 +169,27 @@ def kv_append(w, k_new_fp16: np.ndarray, v_new_fp16: np.ndarray, k_scale=None, v
     if rc != 0:
         raise RuntimeError(f"oracle_kv_append failed with code {rc}")
     return kp, vp
+
+
+def fp16_rne(values) -> np.ndarray:
+    """IEEE binary16 bits (uint16) of each float64 value, rounded to nearest even."""
+    lib = _load()
+    v = np.asarray(values, dtype=np.float64).ravel()
+    return np.array([lib.oracle_fp16_rne(float(x)) for x in v], dtype=np.uint16).reshape(np.shape(values))
+
+
+def dequant(w, pool: Optional[np.ndarray] = None, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Paged E4M3 -> FP16 bridge of workload ``w``'s pool (K by default):
+    float16 [B, capacity, Hkv, D], e4m3(byte) * scale rounded once; +0.0
+    beyond each live length. scale None means 1."""
+    p = np.ascontiguousarray(w.k_pool if pool is None else pool, dtype=np.uint8)
+    sc = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    bt = np.ascontiguousarray(w.block_table, dtype=np.int32)
+    ll = np.ascontiguousarray(w.live_len, dtype=np.int32)
+    out = np.empty((w.batch, w.capacity, w.num_kv_heads, w.head_dim), dtype=np.uint16)
+    rc = _load().oracle_dequant(w.batch, w.num_kv_heads, w.head_dim, w.page_size, w.max_pages_per_row,
+                                w.num_pool_pages, w.page_stride, w.token_stride, w.head_stride, _ptr(p),
+                                _ptr(sc) if sc is not None else None, _ptr(bt), _ptr(ll), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_dequant failed with code {rc}")
+    return out.view(np.float16)

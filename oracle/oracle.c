@@ -374,3 +374,62 @@ int oracle_kv_append(int32_t batch, int32_t q, int32_t num_kv_heads, int32_t hea
     }
     return ORACLE_OK;
 }
+
+/* IEEE binary16 bits of the double v rounded to nearest, ties to even
+ * (overflow to infinity, gradual underflow, NaN -> 0x7E00). */
+uint32_t oracle_fp16_rne(double v) {
+    if (isnan(v)) return 0x7E00u;
+    const uint32_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (a >= 65520.0) return sign | 0x7C00u; /* halfway to 2^16 and above: infinity */
+    if (a < ldexp(1.0, -14)) {
+        const double n = nearbyint(a * 16777216.0); /* multiples of 2^-24; 1024 is the smallest normal */
+        return sign | (uint32_t)n;
+    }
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e -= 1;
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    double sig = nearbyint(a / ldexp(1.0, e - 10)); /* 1024 .. 2048 */
+    if (sig >= 2048.0) {
+        sig = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return sign | 0x7C00u;
+    return sign | (uint32_t)(((e + 15) << 10) | ((int)sig - 1024));
+}
+
+/*
+ * Paged E4M3 -> FP16 bridge ("[Kernel][SM70] Add opt-in E4M3 grouped
+ * attention with FP32 partials", Scope list: the E4M3 paged-to-FP16 bridge
+ * API): out[b][t][g][d] = FP16 bits of e4m3(byte) * scale[g] rounded once to
+ * nearest even for t < live_len[b], +0.0 beyond. scale == NULL means 1.
+ * out is [batch, max_pages_per_row * page_size, num_kv_heads, head_dim].
+ */
+int oracle_dequant(int32_t batch, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                   int32_t max_pages_per_row, int32_t num_pool_pages, int64_t page_stride, int64_t token_stride,
+                   int64_t head_stride, const uint8_t* pool, const float* scale, const int32_t* block_table,
+                   const int32_t* live_len, uint16_t* out) {
+    const int64_t capacity = (int64_t)max_pages_per_row * page_size;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = live_len[b];
+        if (L < 0) L = 0;
+        if (L > capacity) L = capacity;
+        for (int64_t t = 0; t < capacity; ++t) {
+            for (int32_t g = 0; g < num_kv_heads; ++g) {
+                uint16_t* dst = out + ((b * capacity + t) * num_kv_heads + g) * head_dim;
+                if (t >= L) {
+                    for (int32_t d = 0; d < head_dim; ++d) dst[d] = 0;
+                    continue;
+                }
+                const int32_t page = block_table[(int64_t)b * max_pages_per_row + t / page_size];
+                if (page < 0 || page >= num_pool_pages) return ORACLE_ERR_ARG;
+                const uint8_t* src = pool + (int64_t)page * page_stride + (t % page_size) * token_stride +
+                                     (int64_t)g * head_stride;
+                const double s = scale ? (double)scale[g] : 1.0;
+                for (int32_t d = 0; d < head_dim; ++d)
+                    dst[d] = (uint16_t)oracle_fp16_rne(oracle_e4m3_value(src[d]) * s);
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -414,3 +414,40 @@ def test_kv_append_writes_exactly_the_draft_slots():
                                                                                    w.v_scale[g]))
     assert touched.sum() == 4 + 2  # request 1 (L=2 < q=4) writes only its last two rows; request 2 nothing
     assert np.array_equal(view_k[~touched], old_k[~touched])
+
+
+# ---- the scaled E4M3 -> FP16 bridge ----
+
+def test_fp16_rne_matches_numpy_double_to_half():
+    rng = np.random.default_rng(7)
+    halves = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    finite = halves[np.isfinite(halves)]
+    nxt = np.nextafter(finite, np.inf)
+    mids = (finite[:-1] + np.sort(finite)[1:]) / 2
+    x = np.concatenate([finite, (finite + nxt) / 2, mids, rng.normal(0, 1e3, 5000), rng.normal(0, 1e-5, 5000),
+                        [65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -25, 3 * 2.0 ** -25]])
+    got = oracle.fp16_rne(x)
+    assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("scale", [None, 1.0, 0.0011, 3.0e-7, 1.0 + 2.0 ** -12, 2.0 ** -9 * 3])
+def test_dequant_is_one_rounding_of_the_exact_product(scale):
+    w = W.build(seed=71, batch=2, q=2, num_q_heads=2, num_kv_heads=2, head_dim=64, page_size=16,
+                lengths=[40, 5])
+    view = w.pool_view(w.k_pool)
+    codes = np.arange(256, dtype=np.uint8)
+    view[w.block_table[0, 0], :, :, :] = np.resize(codes, view[0].shape)  # every code in request 0's first page
+    sc = None if scale is None else np.array([scale, 2 * scale], dtype=np.float32)
+    got = oracle.dequant(w, scale=sc)
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(2):
+        L = int(w.live_len[b])
+        t = np.arange(L)
+        raw = view[w.block_table[b, t // 16], t % 16]                      # [L, Hkv, D]
+        s = np.ones(2) if sc is None else sc.astype(np.float64)
+        want = (table[raw] * s[None, :, None]).astype(np.float16)          # numpy: one RNE from float64
+        g = got[b, :L]
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(g), nan)
+        assert np.array_equal(g[~nan].view(np.uint16), want[~nan].view(np.uint16))
+        assert np.all(got[b, L:].view(np.uint16) == 0)
