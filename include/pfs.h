@@ -45,7 +45,7 @@ extern "C" {
  * changes. Callers refuse a library whose pfs_abi_version() differs from the
  * header they were built against (the pages' "stale native rejection":
  * "[Bugfix] Use FP32 state ...", Purpose, precision revision / rebuild). */
-#define PFS_ABI_VERSION 1
+#define PFS_ABI_VERSION 2
 
 enum {
     PFS_OK = 0,
@@ -175,13 +175,41 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
  * Scope list: an explicit E4M3 paged-to-FP16 bridge API).
  * Writes out_fp16 as a dense device array [batch, capacity, num_kv_heads,
  * head_dim] (capacity = max_pages_per_row * page_size): element (b, t, g, d)
- * is the exact FP16 value of the pool byte of token t of request b when
- * t < live_len[b], and +0.0 otherwise. Every finite E4M3 value is an FP16
- * normal number or zero, so the conversion is exact; NaN codes give NaN.
- * Same alignment and precondition rules as pfs_verify; no workspace.
+ * is e4m3(byte) * scale[g] rounded once to the nearest FP16 (ties to even)
+ * for the pool byte of token t of request b when t < live_len[b], and +0.0
+ * otherwise. scale is a device [num_kv_heads] FP32 array, or NULL for the
+ * unscaled decode (exact: every finite E4M3 value is an FP16 number). NaN
+ * codes give NaN. Same alignment and precondition rules as pfs_verify; no
+ * workspace. Only the plan's batch, num_kv_heads, head_dim, page size,
+ * max_pages_per_row and strides are used.
  */
-int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
-                          const int32_t* live_len, void* out_fp16, pfs_stream_t stream);
+int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float* scale,
+                          const int32_t* block_table, const int32_t* live_len, void* out_fp16,
+                          pfs_stream_t stream);
+
+/*
+ * Quantize-on-write of the draft tokens (the step before verify: the
+ * draft tokens' K/V enter the paged cache; "[Kernel] Preserve DFlash2
+ * sampling precision and repair QUASAR TP2", Purpose: deferred accepted-slot
+ * writes; "[Bugfix] Use FP32 state and E4M3 defaults for DFlash2", Test
+ * Plan: KV scaling).
+ *   k_new_fp16/v_new_fp16  device [batch, q, num_kv_heads, head_dim] FP16,
+ *                          16-byte aligned: the K and V of each request's q
+ *                          draft tokens, row i being token live_len[b] - q + i
+ *   k_scale/v_scale        device [num_kv_heads] FP32
+ *   k_pool/v_pool          the plan's paged pools, written in place
+ * Each value x is stored as the E4M3FN code nearest to the FP32 quotient
+ * x / scale (IEEE single division), ties to even, saturating at +-448
+ * (infinities included); a NaN quotient stores 0x7F. Rows that would land
+ * before token 0 (live_len[b] < q) are not written; no other byte of the
+ * pools changes. Lengths are clamped into [0, capacity]; block-table entries
+ * of the written tokens must lie in [0, num_pool_pages) (not checked on the
+ * host). Uses the plan's batch, q, num_kv_heads, head_dim, page size and
+ * strides. Enqueue only, no allocation; capturable.
+ */
+int32_t pfs_kv_append(const pfs_plan* plan, const void* k_new_fp16, const void* v_new_fp16,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      const int32_t* live_len, uint8_t* k_pool, uint8_t* v_pool, pfs_stream_t stream);
 
 #ifdef __cplusplus
 }

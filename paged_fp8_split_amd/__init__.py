@@ -12,7 +12,7 @@ from __future__ import annotations
 import math
 from typing import Dict, Optional, Sequence, Tuple
 
-__all__ = ["verify", "dequant_paged", "make_plan", "Plan", "PfsError", "ABI_VERSION"]
+__all__ = ["verify", "dequant_paged", "kv_append", "make_plan", "Plan", "PfsError", "ABI_VERSION"]
 
 _plans: Dict[Tuple, "Plan"] = {}
 
@@ -96,17 +96,42 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     return out
 
 
-def dequant_paged(pool, block_table, live_len, *, out=None, stream=None):
-    """Paged E4M3 pool -> dense float16 [B, capacity, Hkv, D]; tokens at or
-    beyond a request's live length are +0.0."""
+def dequant_paged(pool, block_table, live_len, *, scale=None, out=None, stream=None):
+    """Paged E4M3 pool -> dense float16 [B, capacity, Hkv, D]: each byte's
+    value times ``scale`` (float32 [Hkv], optional) rounded once to FP16;
+    tokens at or beyond a request's live length are +0.0."""
     from . import _lib
     import torch
 
     pages, page, hkv, d, _ = _pool_layout(pool)
     B = int(block_table.shape[0])
+    if scale is not None and (scale.dtype != torch.float32 or not scale.is_contiguous() or scale.numel() != hkv):
+        raise ValueError("scale must be a contiguous float32 tensor [num_kv_heads]")
     plan = make_plan(batch=B, q=1, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=pool,
                      max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0)
     if out is None:
         out = torch.empty((B, plan.capacity, hkv, d), dtype=torch.float16, device=pool.device)
-    _lib.dequant_paged(plan, pool, block_table, live_len, out, stream)
+    _lib.dequant_paged(plan, pool, block_table, live_len, out, stream, scale=scale)
     return out
+
+
+def kv_append(k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, *, stream=None):
+    """Quantize-on-write: store the FP16 K/V [B, q, Hkv, D] of every request's
+    q draft tokens (row i at token live_len[b] - q + i) into the paged E4M3
+    pools, in place: the code nearest to x / scale, ties to even, saturating
+    at +-448. No host synchronization."""
+    from . import _lib
+    import torch
+
+    B, nq, hkv, d = (int(x) for x in k_new.shape)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != torch.float16 or not t.is_contiguous() or tuple(t.shape) != (B, nq, hkv, d):
+            raise ValueError(f"{name} must be a contiguous float16 tensor [B, q, Hkv, D]")
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("K and V pools must share shape and strides")
+    pages, page, phkv, pd, _ = _pool_layout(k_pool)
+    if (phkv, pd) != (hkv, d):
+        raise ValueError("k_new and the pools disagree on num_kv_heads / head_dim")
+    plan = make_plan(batch=B, q=nq, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=k_pool,
+                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0)
+    _lib.kv_append(plan, k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, stream)

@@ -112,7 +112,9 @@ def load():
     lib.pfs_verify_combine.restype = c.c_int32
     lib.pfs_verify_combine.argtypes = [P] * 5 + [c.c_int64, P]
     lib.pfs_dequant_paged.restype = c.c_int32
-    lib.pfs_dequant_paged.argtypes = [P] * 6
+    lib.pfs_dequant_paged.argtypes = [P] * 7
+    lib.pfs_kv_append.restype = c.c_int32
+    lib.pfs_kv_append.argtypes = [P] * 10
     _lib = lib
     return lib
 
@@ -197,9 +199,20 @@ def verify_combine(plan: Plan, v_scale, live_len, out, workspace, stream=None) -
         raise PfsError(st, "pfs_verify_combine")
 
 
-def dequant_paged(plan: Plan, pool, block_table, live_len, out, stream=None) -> None:
-    lib = plan._lib
-    st = lib.pfs_dequant_paged(plan.handle, _ptr(pool), _ptr(block_table), _ptr(live_len), _ptr(out),
-                               _stream_handle(out.device, stream))
+def dequant_paged(plan: Plan, pool, block_table, live_len, out, stream=None, scale=None) -> None:
+    """pfs_dequant_paged: paged E4M3 -> dense FP16 [B, capacity, Hkv, D],
+    times ``scale`` [Hkv] (float32 tensor) rounded once, or unscaled."""
+    st = plan._lib.pfs_dequant_paged(plan.handle, _ptr(pool), None if scale is None else _ptr(scale),
+                                     _ptr(block_table), _ptr(live_len), _ptr(out), _stream_handle(pool.device, stream))
     if st != 0:
         raise PfsError(st, "pfs_dequant_paged")
+
+
+def kv_append(plan: Plan, k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool,
+              stream=None) -> None:
+    """pfs_kv_append: the draft tokens' FP16 K/V [B, q, Hkv, D] -> E4M3 bytes in the pools."""
+    st = plan._lib.pfs_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(block_table), _ptr(live_len), _ptr(k_pool), _ptr(v_pool),
+                                 _stream_handle(k_pool.device, stream))
+    if st != 0:
+        raise PfsError(st, "pfs_kv_append")

@@ -68,5 +68,9 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
                          void* workspace, pfs_stream_t stream);
 int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int32_t* live_len, void* out,
                            const void* workspace, pfs_stream_t stream);
-int32_t pfs_launch_dequant(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
-                           const int32_t* live_len, void* out, pfs_stream_t stream);
+// Implemented in pfs_codec.hip.
+int32_t pfs_launch_append(const pfs_plan* plan, const void* k_new, const void* v_new, const float* k_scale,
+                          const float* v_scale, const int32_t* block_table, const int32_t* live_len,
+                          uint8_t* k_pool, uint8_t* v_pool, pfs_stream_t stream);
+int32_t pfs_launch_bridge(const pfs_plan* plan, const uint8_t* pool, const float* scale, const int32_t* block_table,
+                          const int32_t* live_len, void* out, pfs_stream_t stream);

@@ -2,7 +2,6 @@
 //
 //   e4m3x2_to_f16x2       exact E4M3 -> FP16 dequant-on-load (hardware
 //                         v_cvt_scalef32_pk_f16_fp8 with scale 1.0)
-//   pfs_dequant_kernel    paged E4M3 -> dense FP16 bridge
 //   pfs_split_kernel      per-split QK^T (MFMA), online softmax, PV (MFMA);
 //                         emits FP32 (max, sum, unnormalized PV) per split
 //   pfs_combine_kernel    rescales the splits, sums them in a fixed order
@@ -870,34 +869,6 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const Comb
     for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((num[c] * vs) / lt);
 }
 
-// Paged E4M3 -> dense FP16: one thread per 16 bytes of one (token, KV head).
-__global__ __launch_bounds__(256) void pfs_dequant_kernel(const uint8_t* pool, const int32_t* block_table,
-                                                          const int32_t* live_len, _Float16* out,
-                                                          int64_t page_stride, int64_t token_stride,
-                                                          int64_t head_stride, int32_t num_kv_heads,
-                                                          int32_t head_dim, int32_t page_size, int32_t max_pages,
-                                                          int32_t capacity) {
-    const int chunks = head_dim / 16;
-    const int64_t per_tok = (int64_t)num_kv_heads * chunks;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int b = blockIdx.y;
-    if (idx >= (int64_t)capacity * per_tok) return;
-    const int32_t t = (int32_t)(idx / per_tok);
-    const int g = (int)((idx / chunks) % num_kv_heads);
-    const int c = (int)(idx % chunks);
-    const int32_t L = clamp_i(live_len[b], 0, capacity);
-    u32x4 res[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (t < L) {
-        const int64_t page = block_table[(int64_t)b * max_pages + t / page_size];
-        const u32x4 w = *reinterpret_cast<const u32x4*>(pool + page * page_stride + (int64_t)(t % page_size) * token_stride +
-                                                        (int64_t)g * head_stride + 16 * c);
-        res[0] = bit_cast_<u32x4>(e4m3x8_to_f16x8(w.x, w.y));
-        res[1] = bit_cast_<u32x4>(e4m3x8_to_f16x8(w.z, w.w));
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(out + (((int64_t)b * capacity + t) * num_kv_heads + g) * head_dim + 16 * c);
-    dst[0] = res[0];
-    dst[1] = res[1];
-}
 
 template <int D, int RT, int RG>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
@@ -1009,14 +980,3 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
 
-int32_t pfs_launch_dequant(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
-                           const int32_t* live_len, void* out, pfs_stream_t stream) {
-    const pfs_problem& p = plan->p;
-    const int64_t threads = (int64_t)plan->capacity * p.num_kv_heads * (p.head_dim / 16);
-    const dim3 grid((unsigned)((threads + 255) / 256), p.batch);
-    hipLaunchKernelGGL(pfs_dequant_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), pool,
-                       block_table, live_len, static_cast<_Float16*>(out), p.kv_page_stride, p.kv_token_stride,
-                       p.kv_head_stride, p.num_kv_heads, p.head_dim, p.page_size, p.max_pages_per_row,
-                       plan->capacity);
-    return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
-}

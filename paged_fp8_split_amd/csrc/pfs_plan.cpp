@@ -235,14 +235,30 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
     return pfs_launch_combine(plan, v_scale, live_len, out_fp16, workspace, stream);
 }
 
-int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const int32_t* block_table,
-                          const int32_t* live_len, void* out_fp16, pfs_stream_t stream) {
+int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float* scale,
+                          const int32_t* block_table, const int32_t* live_len, void* out_fp16,
+                          pfs_stream_t stream) {
     if (!plan) return PFS_ERR_NULL;
     if (plan->p.batch == 0) return PFS_OK;
     if (!pool || !block_table || !live_len || !out_fp16) return PFS_ERR_NULL;
     if (((uintptr_t)pool | (uintptr_t)out_fp16) & 15u) return PFS_ERR_ALIGNMENT;
-    if (((uintptr_t)block_table | (uintptr_t)live_len) & 3u) return PFS_ERR_ALIGNMENT;
-    return pfs_launch_dequant(plan, pool, block_table, live_len, out_fp16, stream);
+    if (((uintptr_t)block_table | (uintptr_t)live_len | (uintptr_t)scale) & 3u) return PFS_ERR_ALIGNMENT;
+    return pfs_launch_bridge(plan, pool, scale, block_table, live_len, out_fp16, stream);
+}
+
+int32_t pfs_kv_append(const pfs_plan* plan, const void* k_new_fp16, const void* v_new_fp16, const float* k_scale,
+                      const float* v_scale, const int32_t* block_table, const int32_t* live_len, uint8_t* k_pool,
+                      uint8_t* v_pool, pfs_stream_t stream) {
+    if (!plan) return PFS_ERR_NULL;
+    if (plan->p.batch == 0) return PFS_OK;
+    if (!k_new_fp16 || !v_new_fp16 || !k_scale || !v_scale || !block_table || !live_len || !k_pool || !v_pool)
+        return PFS_ERR_NULL;
+    if (((uintptr_t)k_new_fp16 | (uintptr_t)v_new_fp16 | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15u)
+        return PFS_ERR_ALIGNMENT;
+    if (((uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)block_table | (uintptr_t)live_len) & 3u)
+        return PFS_ERR_ALIGNMENT;
+    return pfs_launch_append(plan, k_new_fp16, v_new_fp16, k_scale, v_scale, block_table, live_len, k_pool, v_pool,
+                             stream);
 }
 
 }  // extern "C"

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = header_functions()
     assert names == sorted([
-        "pfs_abi_version", "pfs_dequant_paged", "pfs_plan_create", "pfs_plan_destroy", "pfs_plan_num_splits",
+        "pfs_abi_version", "pfs_dequant_paged", "pfs_kv_append", "pfs_plan_create", "pfs_plan_destroy",
+        "pfs_plan_num_splits",
         "pfs_plan_tokens_per_split", "pfs_plan_workspace_bytes", "pfs_status_string", "pfs_verify",
         "pfs_verify_combine", "pfs_verify_split"])
     for n in names:
