@@ -58,24 +58,53 @@ def _load():
     lib.oracle_fp16_value.argtypes = [c.c_uint32]
     lib.oracle_e4m3_table.restype = None
     lib.oracle_e4m3_table.argtypes = [P]
+    lib.oracle_e5m2_value.restype = c.c_double
+    lib.oracle_e5m2_value.argtypes = [c.c_uint32]
+    lib.oracle_kv_table.restype = c.c_int
+    lib.oracle_kv_table.argtypes = [c.c_int32, P]
     lib.oracle_visible_keys.restype = c.c_int64
     lib.oracle_visible_keys.argtypes = [c.c_int64, c.c_int32, c.c_int32]
     lib.oracle_max_threads.restype = c.c_int32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_verify.restype = c.c_int
-    lib.oracle_verify.argtypes = [c.c_int32] * 9 + [c.c_int64] * 3 + [P] * 9 + [c.c_double, P, c.c_int32]
+    lib.oracle_verify.argtypes = [c.c_int32] * 9 + [c.c_int64] * 3 + [P] * 9 + [c.c_double, P, c.c_int32, c.c_int32]
     lib.oracle_e4m3_encode.restype = c.c_uint32
     lib.oracle_e4m3_encode.argtypes = [c.c_float]
+    lib.oracle_e5m2_encode.restype = c.c_uint32
+    lib.oracle_e5m2_encode.argtypes = [c.c_float]
     lib.oracle_quantize_fp16.restype = c.c_uint32
-    lib.oracle_quantize_fp16.argtypes = [c.c_uint32, c.c_float]
+    lib.oracle_quantize_fp16.argtypes = [c.c_uint32, c.c_float, c.c_int32]
     lib.oracle_fp16_rne.restype = c.c_uint32
     lib.oracle_fp16_rne.argtypes = [c.c_double]
     lib.oracle_dequant.restype = c.c_int
-    lib.oracle_dequant.argtypes = [c.c_int32] * 6 + [c.c_int64] * 3 + [P] * 5
+    lib.oracle_dequant.argtypes = [c.c_int32] * 6 + [c.c_int64] * 3 + [P] * 5 + [c.c_int32]
     lib.oracle_kv_append.restype = c.c_int
-    lib.oracle_kv_append.argtypes = [c.c_int32] * 7 + [c.c_int64] * 3 + [P] * 8
+    lib.oracle_kv_append.argtypes = [c.c_int32] * 7 + [c.c_int64] * 3 + [P] * 8 + [c.c_int32]
     _lib = lib
     return lib
+
+
+KV_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _fmt(name: str) -> int:
+    try:
+        return KV_FORMATS[name]
+    except KeyError:
+        raise ValueError(f"unknown KV format {name!r}") from None
+
+
+def kv_table(kv_format: str = "e4m3") -> np.ndarray:
+    """Decoded value of every byte 0..255 of a KV format (float64)."""
+    out = np.empty(256, dtype=np.float64)
+    if _load().oracle_kv_table(_fmt(kv_format), out.ctypes.data) != 0:
+        raise ValueError(kv_format)
+    return out
+
+
+def e5m2_table() -> np.ndarray:
+    """Decoded value of every E5M2 byte 0..255 (float64; +-inf and NaN codes included)."""
+    return np.array([_load().oracle_e5m2_value(b) for b in range(256)], dtype=np.float64)
 
 
 def e4m3_table() -> np.ndarray:
@@ -128,7 +157,8 @@ def verify(w, *, partition_tokens: Optional[int] = None, unit_mask: Optional[np.
         w.num_pool_pages, T, w.page_stride, w.token_stride, w.head_stride,
         _ptr(qb), _ptr(kp), _ptr(vp), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(ll), _ptr(hm),
         _ptr(mask) if mask is not None else None,
-        float(w.sm_scale if sm_scale is None else sm_scale), _ptr(out), int(threads))
+        float(w.sm_scale if sm_scale is None else sm_scale), _ptr(out), int(threads),
+        _fmt(getattr(w, "kv_format", "e4m3")))
     if rc != 0:
         raise RuntimeError(f"oracle_verify failed with code {rc}")
     return out
@@ -142,12 +172,21 @@ def e4m3_encode(values) -> np.ndarray:
     return np.array([lib.oracle_e4m3_encode(float(x)) for x in v], dtype=np.uint8).reshape(np.shape(values))
 
 
-def quantize_fp16(bits, scale: float) -> np.ndarray:
-    """E4M3 code of (float)x / scale for FP16 bit patterns ``bits``."""
+def e5m2_encode(values) -> np.ndarray:
+    """E5M2 code (uint8) of each FP32 value: nearest, ties to even,
+    saturating at +-57344, NaN -> 0x7F."""
     lib = _load()
+    v = np.asarray(values, dtype=np.float32).ravel()
+    return np.array([lib.oracle_e5m2_encode(float(x)) for x in v], dtype=np.uint8).reshape(np.shape(values))
+
+
+def quantize_fp16(bits, scale: float, kv_format: str = "e4m3") -> np.ndarray:
+    """Code of (float)x / scale in ``kv_format`` for FP16 bit patterns ``bits``."""
+    lib = _load()
+    f = _fmt(kv_format)
     b = np.asarray(bits, dtype=np.uint16).ravel()
     s = float(np.float32(scale))
-    return np.array([lib.oracle_quantize_fp16(int(x), s) for x in b], dtype=np.uint8).reshape(np.shape(bits))
+    return np.array([lib.oracle_quantize_fp16(int(x), s, f) for x in b], dtype=np.uint8).reshape(np.shape(bits))
 
 
 def kv_append(w, k_new_fp16: np.ndarray, v_new_fp16: np.ndarray, k_scale=None, v_scale=None):
@@ -165,7 +204,7 @@ def kv_append(w, k_new_fp16: np.ndarray, v_new_fp16: np.ndarray, k_scale=None, v
     rc = _load().oracle_kv_append(
         w.batch, w.q, w.num_kv_heads, w.head_dim, w.page_size, w.max_pages_per_row, w.num_pool_pages,
         w.page_stride, w.token_stride, w.head_stride, _ptr(kn), _ptr(vn), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(ll),
-        _ptr(kp), _ptr(vp))
+        _ptr(kp), _ptr(vp), _fmt(getattr(w, "kv_format", "e4m3")))
     if rc != 0:
         raise RuntimeError(f"oracle_kv_append failed with code {rc}")
     return kp, vp
@@ -179,9 +218,10 @@ def fp16_rne(values) -> np.ndarray:
 
 
 def dequant(w, pool: Optional[np.ndarray] = None, scale: Optional[np.ndarray] = None) -> np.ndarray:
-    """Paged E4M3 -> FP16 bridge of workload ``w``'s pool (K by default):
-    float16 [B, capacity, Hkv, D], e4m3(byte) * scale rounded once; +0.0
-    beyond each live length. scale None means 1."""
+    """Paged FP8 -> FP16 bridge of workload ``w``'s pool (K by default):
+    float16 [B, capacity, Hkv, D], dec(byte) * scale rounded once, with dec
+    the decoder of the workload's KV format; +0.0 beyond each live length.
+    scale None means 1."""
     p = np.ascontiguousarray(w.k_pool if pool is None else pool, dtype=np.uint8)
     sc = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
     bt = np.ascontiguousarray(w.block_table, dtype=np.int32)
@@ -189,7 +229,8 @@ def dequant(w, pool: Optional[np.ndarray] = None, scale: Optional[np.ndarray] = 
     out = np.empty((w.batch, w.capacity, w.num_kv_heads, w.head_dim), dtype=np.uint16)
     rc = _load().oracle_dequant(w.batch, w.num_kv_heads, w.head_dim, w.page_size, w.max_pages_per_row,
                                 w.num_pool_pages, w.page_stride, w.token_stride, w.head_stride, _ptr(p),
-                                _ptr(sc) if sc is not None else None, _ptr(bt), _ptr(ll), _ptr(out))
+                                _ptr(sc) if sc is not None else None, _ptr(bt), _ptr(ll), _ptr(out),
+                                _fmt(getattr(w, "kv_format", "e4m3")))
     if rc != 0:
         raise RuntimeError(f"oracle_dequant failed with code {rc}")
     return out.view(np.float16)

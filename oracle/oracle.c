@@ -82,6 +82,41 @@ void oracle_e4m3_table(double* out) {
     for (uint32_t b = 0; b < 256; ++b) out[b] = oracle_e4m3_value(b);
 }
 
+/* E5M2 byte -> exact value: the IEEE-style 8-bit format with a 5-bit
+ * exponent (bias 15) and a 2-bit mantissa, kept beside E4M3 as an explicit
+ * alternative KV format ("[Bugfix] Use FP32 state and E4M3 defaults for
+ * DFlash2", Purpose: E4M3 is the default, E5M2 stays available on request;
+ * "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+ * historical scope: explicit E5M2 routes are kept). e == 0 is subnormal:
+ * m/4 * 2^(1-15); e == 31 is infinity (m == 0) or NaN; otherwise
+ * (1 + m/4) * 2^(e-15). Largest finite value 57344. */
+double oracle_e5m2_value(uint32_t byte) {
+    const int s = (int)((byte >> 7) & 1u);
+    const int e = (int)((byte >> 2) & 31u);
+    const int m = (int)(byte & 3u);
+    double mag;
+    if (e == 31) {
+        if (m) return NAN;
+        return s ? -INFINITY : INFINITY;
+    }
+    if (e == 0)
+        mag = ldexp((double)m / 4.0, 1 - 15);
+    else
+        mag = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -mag : mag;
+}
+
+#define ORACLE_KV_E4M3 0
+#define ORACLE_KV_E5M2 1
+
+/* Decoded value of every byte of KV format `format`; 0 on success. */
+int oracle_kv_table(int32_t format, double* out) {
+    if (format != ORACLE_KV_E4M3 && format != ORACLE_KV_E5M2) return ORACLE_ERR_ARG;
+    for (uint32_t b = 0; b < 256; ++b)
+        out[b] = format == ORACLE_KV_E5M2 ? oracle_e5m2_value(b) : oracle_e4m3_value(b);
+    return ORACLE_OK;
+}
+
 /* Number of keys draft row i of a request with live length L may attend to. */
 int64_t oracle_visible_keys(int64_t live_len, int32_t q, int32_t row) {
     int64_t n = live_len - (int64_t)q + (int64_t)row + 1;
@@ -105,6 +140,9 @@ int64_t oracle_visible_keys(int64_t live_len, int32_t q, int32_t row) {
  *               byte is non-zero (others are left untouched)
  *   out         [batch, q, num_q_heads, head_dim] FP64 (unrounded result)
  *
+ * kv_format selects how the pool bytes decode: 0 = E4M3FN (the default
+ * format of the method), 1 = E5M2.
+ *
  * partition_tokens <= 0 means a single partition per row (the unsplit
  * softmax). Returns ORACLE_OK or a negative error code.
  */
@@ -115,7 +153,7 @@ int oracle_verify(int32_t batch, int32_t q, int32_t num_q_heads, int32_t num_kv_
                   const uint8_t* k_pool, const uint8_t* v_pool, const float* k_scale,
                   const float* v_scale, const int32_t* block_table, const int32_t* live_len,
                   const int32_t* head_map, const uint8_t* unit_mask, double sm_scale,
-                  double* out, int32_t num_threads) {
+                  double* out, int32_t num_threads, int32_t kv_format) {
     if (batch < 0 || q < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
         page_size < 1 || max_pages_per_row < 0 || num_pool_pages < 0)
         return ORACLE_ERR_ARG;
@@ -126,7 +164,7 @@ int oracle_verify(int32_t batch, int32_t q, int32_t num_q_heads, int32_t num_kv_
         if (head_map[h] < 0 || head_map[h] >= num_kv_heads) return ORACLE_ERR_ARG;
 
     double table[256];
-    oracle_e4m3_table(table);
+    if (oracle_kv_table(kv_format, table) != ORACLE_OK) return ORACLE_ERR_ARG;
 
     const int64_t capacity = (int64_t)max_pages_per_row * page_size;
     const int64_t units = (int64_t)batch * num_q_heads;
@@ -332,11 +370,37 @@ uint32_t oracle_e4m3_encode(float v) {
     return sign | (uint32_t)(((e + 7) << 3) | ((int)sig - 8));
 }
 
-/* FP16 bits x stored with scale s: the code of (float)x / s. */
-uint32_t oracle_quantize_fp16(uint32_t bits, float scale) {
+/* E5M2 code nearest to the FP32 value v, ties to even, saturating at
+ * +-57344 (infinities too); NaN -> 0x7F (a NaN code of E5M2 as well). The
+ * same reading as the E4M3 encoder, on E5M2's grid: normals (1 + m/4) *
+ * 2^e for e in [-14, 15], subnormals multiples of 2^-16. */
+uint32_t oracle_e5m2_encode(float v) {
+    if (isnan(v)) return 0x7Fu;
+    const uint32_t sign = signbit(v) ? 0x80u : 0u;
+    const double a = fabs((double)v);
+    if (a >= 57344.0) return sign | 0x7Bu; /* 57344 = S.11110.11 */
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal grid: multiples of 2^-16; rounding to 4 gives the smallest normal */
+        const double n = nearbyint(a * 65536.0);
+        return sign | (uint32_t)n;
+    }
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e -= 1;
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    double sig = nearbyint(a / ldexp(1.0, e - 2)); /* 4 .. 8 */
+    if (sig >= 8.0) {
+        sig = 4.0;
+        e += 1;
+    }
+    if (e > 15 || (e == 15 && sig > 7.0)) return sign | 0x7Bu;
+    return sign | (uint32_t)(((e + 15) << 2) | ((int)sig - 4));
+}
+
+/* FP16 bits x stored with scale s in KV format `format`: the code of (float)x / s. */
+uint32_t oracle_quantize_fp16(uint32_t bits, float scale, int32_t format) {
     const float x = (float)oracle_fp16_value(bits);
     const float quotient = x / scale;
-    return oracle_e4m3_encode(quotient);
+    return format == ORACLE_KV_E5M2 ? oracle_e5m2_encode(quotient) : oracle_e4m3_encode(quotient);
 }
 
 /*
@@ -344,13 +408,16 @@ uint32_t oracle_quantize_fp16(uint32_t bits, float scale) {
  *   k_new/v_new [batch, q, num_kv_heads, head_dim] IEEE half bit patterns
  *   pools, strides, block_table, live_len as for oracle_verify; lengths are
  *   clamped into [0, max_pages_per_row * page_size].
- * Returns ORACLE_OK, or ORACLE_ERR_ARG for a block-table entry outside the pool.
+ *   kv_format 0 stores E4M3FN codes, 1 stores E5M2 codes.
+ * Returns ORACLE_OK, or ORACLE_ERR_ARG for a block-table entry outside the
+ * pool or an unknown format.
  */
 int oracle_kv_append(int32_t batch, int32_t q, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                      int32_t max_pages_per_row, int32_t num_pool_pages, int64_t page_stride,
                      int64_t token_stride, int64_t head_stride, const uint16_t* k_new, const uint16_t* v_new,
                      const float* k_scale, const float* v_scale, const int32_t* block_table,
-                     const int32_t* live_len, uint8_t* k_pool, uint8_t* v_pool) {
+                     const int32_t* live_len, uint8_t* k_pool, uint8_t* v_pool, int32_t kv_format) {
+    if (kv_format != ORACLE_KV_E4M3 && kv_format != ORACLE_KV_E5M2) return ORACLE_ERR_ARG;
     const int64_t capacity = (int64_t)max_pages_per_row * page_size;
     for (int32_t b = 0; b < batch; ++b) {
         int64_t L = live_len[b];
@@ -366,8 +433,8 @@ int oracle_kv_append(int32_t batch, int32_t q, int32_t num_kv_heads, int32_t hea
                 const int64_t src = (((int64_t)b * q + i) * num_kv_heads + g) * head_dim;
                 for (int32_t d = 0; d < head_dim; ++d) {
                     const int64_t dst = base + (int64_t)g * head_stride + d;
-                    k_pool[dst] = (uint8_t)oracle_quantize_fp16(k_new[src + d], k_scale[g]);
-                    v_pool[dst] = (uint8_t)oracle_quantize_fp16(v_new[src + d], v_scale[g]);
+                    k_pool[dst] = (uint8_t)oracle_quantize_fp16(k_new[src + d], k_scale[g], kv_format);
+                    v_pool[dst] = (uint8_t)oracle_quantize_fp16(v_new[src + d], v_scale[g], kv_format);
                 }
             }
         }
@@ -401,14 +468,17 @@ uint32_t oracle_fp16_rne(double v) {
 /*
  * Paged E4M3 -> FP16 bridge ("[Kernel][SM70] Add opt-in E4M3 grouped
  * attention with FP32 partials", Scope list: the E4M3 paged-to-FP16 bridge
- * API): out[b][t][g][d] = FP16 bits of e4m3(byte) * scale[g] rounded once to
- * nearest even for t < live_len[b], +0.0 beyond. scale == NULL means 1.
+ * API): out[b][t][g][d] = FP16 bits of dec(byte) * scale[g] rounded once to
+ * nearest even for t < live_len[b], +0.0 beyond, with dec the decoder of
+ * kv_format (0 = E4M3FN, 1 = E5M2). scale == NULL means 1.
  * out is [batch, max_pages_per_row * page_size, num_kv_heads, head_dim].
  */
 int oracle_dequant(int32_t batch, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                    int32_t max_pages_per_row, int32_t num_pool_pages, int64_t page_stride, int64_t token_stride,
                    int64_t head_stride, const uint8_t* pool, const float* scale, const int32_t* block_table,
-                   const int32_t* live_len, uint16_t* out) {
+                   const int32_t* live_len, uint16_t* out, int32_t kv_format) {
+    double table[256];
+    if (oracle_kv_table(kv_format, table) != ORACLE_OK) return ORACLE_ERR_ARG;
     const int64_t capacity = (int64_t)max_pages_per_row * page_size;
     for (int32_t b = 0; b < batch; ++b) {
         int64_t L = live_len[b];
@@ -427,7 +497,7 @@ int oracle_dequant(int32_t batch, int32_t num_kv_heads, int32_t head_dim, int32_
                                      (int64_t)g * head_stride;
                 const double s = scale ? (double)scale[g] : 1.0;
                 for (int32_t d = 0; d < head_dim; ++d)
-                    dst[d] = (uint16_t)oracle_fp16_rne(oracle_e4m3_value(src[d]) * s);
+                    dst[d] = (uint16_t)oracle_fp16_rne(table[src[d]] * s);
             }
         }
     }

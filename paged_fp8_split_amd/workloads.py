@@ -28,6 +28,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 SENTINEL_NAN = 0x7F  # the E4M3 NaN byte; fills every byte no live token owns
 SENTINEL_MAX = 0x7E  # 448.0, the alternative tail sentinel used by tests
 
@@ -58,6 +59,7 @@ class Workload:
     head_map: np.ndarray  # int32 [Hq]
     sm_scale: float
     partition_tokens: int = 64
+    kv_format: str = "e4m3"  # how the pool bytes encode values: "e4m3" (E4M3FN) or "e5m2"
     notes: dict = dataclasses.field(default_factory=dict)
 
     @property
@@ -99,6 +101,22 @@ def _e4m3_bytes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
+def _e5m2_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 array -> E5M2 bytes: clamp to +-57344, then torch's RNE encoder."""
+    import torch
+
+    x = np.clip(np.asarray(x, dtype=np.float32), -E5M2_MAX, E5M2_MAX)
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy().copy()
+
+
+# per format: largest finite value, encoder, and the codes of 1.0 and of the next larger value
+_FORMATS = {
+    "e4m3": (E4M3_MAX, _e4m3_bytes, 0x38, 0x39),
+    "e5m2": (E5M2_MAX, _e5m2_bytes, 0x3C, 0x3D),
+}
+
+
 def build(
     *,
     batch: int,
@@ -120,6 +138,7 @@ def build(
     sentinel: int = SENTINEL_NAN,
     zero_k_heads: Sequence[tuple] = (),
     midpoint: Optional[dict] = None,
+    kv_format: str = "e4m3",
     name: str = "custom",
 ) -> Workload:
     """Build a seeded verify-attention workload.
@@ -133,9 +152,15 @@ def build(
     token_pad / page_pad: extra bytes added to the token / page stride.
     zero_k_heads: (b, g) pairs whose live K bytes are all 0x00 (all scores 0).
     midpoint: {"b": b, "g": g, "counts": [c_0, c_1, ...]}; for that slot the V
-        bytes are 0x38 (1.0) except counts[d % len(counts)] tokens of column d,
-        which are 0x39 (1.125); its K bytes are 0x00.
+        bytes are the code of 1.0 except counts[d % len(counts)] tokens of
+        column d, which hold the next larger value (E4M3: 0x38 = 1.0 and
+        0x39 = 1.125); its K bytes are 0x00.
+    kv_format: "e4m3" (E4M3FN bytes, scales absmax/448) or "e5m2" (E5M2
+        bytes, scales absmax/57344).
     """
+    if kv_format not in _FORMATS:
+        raise ValueError(f"unknown kv_format {kv_format!r}")
+    fmax, encode, code_one, code_next = _FORMATS[kv_format]
     B, Hq, Hkv, D, P = batch, num_q_heads, num_kv_heads, head_dim, page_size
     if Hq % Hkv:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
@@ -199,14 +224,14 @@ def build(
         else:
             raise ValueError(f"unknown scale_mode {scale_mode!r}")
         amax = np.where(amax > 0, amax, 1.0).astype(np.float32)
-        return (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        return (amax / np.float32(fmax)).astype(np.float32)
 
     def fill(pool, x, scale):
         view = np.lib.stride_tricks.as_strided(
             pool, shape=(num_pool, P, Hkv, D), strides=(page_stride, token_stride, head_stride, 1), writeable=True
         )
         if n_tok:
-            view[tok_page, tok_slot] = _e4m3_bytes(x / scale[None, :, None])
+            view[tok_page, tok_slot] = encode(x / scale[None, :, None])
 
     xk = draw(r_k)
     k_scale = scales_for(xk)
@@ -232,10 +257,10 @@ def build(
         sel = np.nonzero(tok_b == b)[0]
         L = len(sel)
         kview[tok_page[sel], tok_slot[sel], g] = 0x00
-        col = np.full((L, D), 0x38, dtype=np.uint8)
+        col = np.full((L, D), code_one, dtype=np.uint8)
         for d in range(D):
             c = counts[d % len(counts)]
-            col[r_misc.choice(L, size=c, replace=False), d] = 0x39
+            col[r_misc.choice(L, size=c, replace=False), d] = code_next
         vview[tok_page[sel], tok_slot[sel], g] = col
         notes["midpoint"] = {"b": b, "g": g, "counts": counts}
 
@@ -262,6 +287,7 @@ def build(
         live_len=lengths.astype(np.int32),
         head_map=(np.arange(Hq) // (Hq // Hkv)).astype(np.int32),
         sm_scale=1.0 / math.sqrt(D),
+        kv_format=kv_format,
         notes=notes,
     )
 
@@ -376,4 +402,5 @@ def device_tensors(w: Workload, device) -> dict:
         "live_len": torch.from_numpy(w.live_len.copy()).to(device),
         "head_map": [int(x) for x in w.head_map],
         "sm_scale": float(w.sm_scale),
+        "kv_format": w.kv_format,
     }

@@ -64,7 +64,8 @@ def _dense_kv(w, pool, scale, b, g, L):
     view = w.pool_view(pool)
     t = np.arange(L)
     raw = np.ascontiguousarray(view[w.block_table[b, t // w.page_size], t % w.page_size, g])
-    dec = torch.from_numpy(raw).view(torch.float8_e4m3fn).to(torch.float64)
+    fp8 = torch.float8_e5m2 if w.kv_format == "e5m2" else torch.float8_e4m3fn
+    dec = torch.from_numpy(raw).view(fp8).to(torch.float64)
     return dec * float(scale[g])
 
 
@@ -390,9 +391,10 @@ def test_quantize_fp16_is_the_code_of_the_fp32_quotient(scale):
     assert np.array_equal(got[~big], _torch_e4m3_codes(q32[~big]))
 
 
-def test_kv_append_writes_exactly_the_draft_slots():
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_kv_append_writes_exactly_the_draft_slots(kv_format):
     w = W.build(seed=61, batch=3, q=4, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
-                lengths=[37, 2, 0])
+                lengths=[37, 2, 0], kv_format=kv_format)
     rng = np.random.default_rng(62)
     kn = rng.normal(0, 3, (3, 4, 2, 64)).astype(np.float16)
     vn = rng.normal(0, 3, (3, 4, 2, 64)).astype(np.float16)
@@ -409,9 +411,9 @@ def test_kv_append_writes_exactly_the_draft_slots():
             touched[page, slot] = True
             for g in range(2):
                 assert np.array_equal(view_k[page, slot, g], oracle.quantize_fp16(kn[b, i, g].view(np.uint16),
-                                                                                   w.k_scale[g]))
+                                                                                   w.k_scale[g], kv_format))
                 assert np.array_equal(view_v[page, slot, g], oracle.quantize_fp16(vn[b, i, g].view(np.uint16),
-                                                                                   w.v_scale[g]))
+                                                                                   w.v_scale[g], kv_format))
     assert touched.sum() == 4 + 2  # request 1 (L=2 < q=4) writes only its last two rows; request 2 nothing
     assert np.array_equal(view_k[~touched], old_k[~touched])
 
@@ -430,16 +432,18 @@ def test_fp16_rne_matches_numpy_double_to_half():
     assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("scale", [None, 1.0, 0.0011, 3.0e-7, 1.0 + 2.0 ** -12, 2.0 ** -9 * 3])
-def test_dequant_is_one_rounding_of_the_exact_product(scale):
+def test_dequant_is_one_rounding_of_the_exact_product(scale, kv_format):
     w = W.build(seed=71, batch=2, q=2, num_q_heads=2, num_kv_heads=2, head_dim=64, page_size=16,
-                lengths=[40, 5])
+                lengths=[40, 5], kv_format=kv_format)
     view = w.pool_view(w.k_pool)
     codes = np.arange(256, dtype=np.uint8)
     view[w.block_table[0, 0], :, :, :] = np.resize(codes, view[0].shape)  # every code in request 0's first page
     sc = None if scale is None else np.array([scale, 2 * scale], dtype=np.float32)
     got = oracle.dequant(w, scale=sc)
-    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fp8 = torch.float8_e5m2 if kv_format == "e5m2" else torch.float8_e4m3fn
+    table = torch.arange(256, dtype=torch.uint8).view(fp8).to(torch.float64).numpy()
     for b in range(2):
         L = int(w.live_len[b])
         t = np.arange(L)
@@ -451,3 +455,109 @@ def test_dequant_is_one_rounding_of_the_exact_product(scale):
         assert np.array_equal(np.isnan(g), nan)
         assert np.array_equal(g[~nan].view(np.uint16), want[~nan].view(np.uint16))
         assert np.all(got[b, L:].view(np.uint16) == 0)
+
+
+# ---- the E5M2 KV format (the explicit alternative to E4M3) ----
+
+def test_e5m2_decode_matches_torch_and_the_fp16_high_byte():
+    ours = oracle.e5m2_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    # an E5M2 byte is the high byte of the IEEE half with the same value
+    half = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(half))
+    assert np.array_equal(ours[fin], half[fin])
+    assert np.array_equal(oracle.kv_table("e5m2")[fin], ours[fin])
+
+
+def test_e5m2_range_and_special_codes():
+    t = oracle.e5m2_table()
+    assert t[0x7B] == 57344.0 and t[0xFB] == -57344.0
+    assert t[0x7C] == np.inf and t[0xFC] == -np.inf
+    assert np.isnan(t).sum() == 6  # 0x7D..0x7F and 0xFD..0xFF
+    assert t[0x01] == 2.0 ** -16 and t[0x04] == 2.0 ** -14
+    assert t[0x3C] == 1.0 and t[0x3D] == 1.25
+
+
+def _torch_e5m2_codes(v32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e5m2 conversion (round to nearest even) of
+    values already clamped to +-57344."""
+    t = torch.from_numpy(np.clip(v32.astype(np.float32), -57344.0, 57344.0))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_e5m2_encode_round_trips_every_finite_code():
+    table = oracle.e5m2_table()
+    finite = [b for b in range(256) if np.isfinite(table[b])]
+    got = oracle.e5m2_encode(table[finite].astype(np.float32))
+    assert np.array_equal(got, np.array(finite, dtype=np.uint8))
+
+
+def test_e5m2_encode_matches_torch_and_brute_force_nearest():
+    rng = np.random.default_rng(15)
+    table = oracle.e5m2_table()
+    codes = np.array([b for b in range(256) if np.isfinite(table[b])])
+    vals = table[codes]
+    mids = ((vals[:, None] + vals[None, :]) / 2).ravel()
+    x = np.concatenate([
+        rng.normal(0, 1, 4000), rng.normal(0, 5000, 2000), rng.uniform(-2 ** -14, 2 ** -14, 2000),
+        mids[np.abs(mids) <= 57344], [0.0, -0.0, 57344.0, -57344.0, 2 ** -17, -(2 ** -17), 3 * 2 ** -17],
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 57344]
+    got = oracle.e5m2_encode(x)
+    assert np.array_equal(got, _torch_e5m2_codes(x))
+    for v, c in zip(x[:3000], got[:3000]):
+        if float(v) == 0.0:
+            continue
+        d = np.abs(vals - float(v))
+        best = codes[d == d.min()]
+        best = best[best % 2 == 0] if len(best) > 1 else best
+        assert c == best[0] or (table[c] == table[best[0]]), (v, c, best)
+    assert oracle.e5m2_encode(np.float32(-0.0)) == 0x80 and oracle.e5m2_encode(np.float32(0.0)) == 0x00
+
+
+def test_e5m2_encode_saturates_and_maps_nan():
+    big = np.array([57344.0, 57345.0, 61439.0, 61440.0, 65504.0, 1.0e30, np.inf], dtype=np.float32)
+    assert np.all(oracle.e5m2_encode(big) == 0x7B)
+    assert np.all(oracle.e5m2_encode(-big) == 0xFB)
+    assert oracle.e5m2_encode(np.float32(np.nan)) == 0x7F
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 2.0 ** -10, 1000.0])
+def test_quantize_fp16_e5m2_is_the_code_of_the_fp32_quotient(scale):
+    bits = np.arange(0, 65536, 5, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16).astype(np.float32)
+    keep = np.isfinite(x)
+    q32 = (x[keep] / np.float32(scale)).astype(np.float32)
+    got = oracle.quantize_fp16(bits[keep], scale, "e5m2")
+    big = np.abs(q32) > 57344
+    assert np.all(got[big & (q32 > 0)] == 0x7B) and np.all(got[big & (q32 < 0)] == 0xFB)
+    assert np.array_equal(got[~big], _torch_e5m2_codes(q32[~big]))
+
+
+@pytest.mark.parametrize("case", [1, 2, 4])
+def test_oracle_matches_torch_sdpa_e5m2(case):
+    w = W.build(seed=300 + case, kv_format="e5m2", **SMALL[case])
+    ours = oracle.verify(w)
+    assert np.all(np.isfinite(ours))
+    assert _rel(ours, sdpa_reference(w)) < 1e-13
+
+
+def test_oracle_e5m2_with_outliers_and_pow2_scales():
+    w = W.build(seed=8, batch=2, q=8, num_q_heads=8, num_kv_heads=4, head_dim=32, page_size=16,
+                lengths=[260, 97], outlier_frac=0.05, scale_mode="pow2", pow2_scale_exps=[-14, -6, 1, 4],
+                kv_format="e5m2")
+    assert _rel(oracle.verify(w), sdpa_reference(w)) < 1e-13
+
+
+def test_oracle_reads_the_format_it_is_given():
+    # the same bytes read as the other format give another result (the format is not ignored)
+    w = W.build(seed=9, batch=1, q=2, num_q_heads=2, num_kv_heads=1, head_dim=16, page_size=16, lengths=[40])
+    w.k_pool &= 0xBF  # clear bit 6: every byte is then finite in both formats
+    w.v_pool &= 0xBF
+    w2 = w.copy()
+    w2.kv_format = "e5m2"
+    assert _rel(oracle.verify(w2), oracle.verify(w)) > 1e-3
+    assert _rel(oracle.verify(w2), sdpa_reference(w2)) < 1e-13
