@@ -82,6 +82,133 @@ def split_algorithmic_bytes(w, plan) -> int:
     return kv + qb + bt + ws
 
 
+def codec_timing(w, t, dev, evict, reps: int = 20) -> dict:
+    """The two codec kernels on the same workload, HIP events on the current
+    stream: the draft-token quantize-on-write (q rows x KV heads, launch
+    bound) and the scaled paged E4M3 -> FP16 bridge over every live token of
+    the K pool (cache scrubbed before each launch). Runs last: the append
+    writes the draft slots of the pools."""
+    import numpy as np
+    import torch
+
+    import paged_fp8_split_amd as pfs
+
+    rng = np.random.default_rng(12)
+    shape = (w.batch, w.q, w.num_kv_heads, w.head_dim)
+    kn = torch.from_numpy(rng.normal(0, 1, shape).astype(np.float16)).to(dev)
+    vn = torch.from_numpy(rng.normal(0, 1, shape).astype(np.float16)).to(dev)
+    out = torch.empty((w.batch, w.capacity, w.num_kv_heads, w.head_dim), dtype=torch.float16, device=dev)
+
+    def timed(fn, scrub):
+        ms = []
+        for k in range(reps + 3):
+            if scrub:
+                evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if k >= 3:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms)) * 1e3
+
+    # the append is a few microseconds of GPU work: time a graph of `chain`
+    # back-to-back appends (idempotent) so that neither the binding's host
+    # overhead nor the graph launch is inside the per-append figure
+    append = lambda: pfs.kv_append(kn, vn, t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
+                                   t["k_pool"], t["v_pool"])
+    append()
+    torch.cuda.synchronize()
+    chain = 50
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(chain):
+            append()
+    torch.cuda.synchronize()
+    app_us = timed(graph.replay, False) / chain
+    br_us = timed(lambda: pfs.dequant_paged(t["k_pool"], t["block_table"], t["live_len"], scale=t["k_scale"],
+                                            out=out), True)
+    live = int(np.clip(w.live_len.astype(np.int64), 0, w.capacity).sum())
+    br_bytes = live * w.num_kv_heads * w.head_dim * 3 + (w.batch * w.capacity - live) * w.num_kv_heads * w.head_dim * 2
+    app_bytes = int(np.prod(shape)) * (2 * 2 + 2)
+    return {
+        "kv_append_us": round(app_us, 2),  # per append in a graph of back-to-back appends
+        "kv_append_bytes": app_bytes,
+        "bridge_scaled_us": round(br_us, 2),
+        "bridge_bytes": br_bytes,
+        "bridge_GBps": round(br_bytes / (br_us * 1e-6) / 1e9, 1),
+        "bridge_frac_of_peak": round(br_bytes / (br_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
+def time_steps(split, combine, evict, stream, steps: int, warmup: int):
+    """Warm up, then time `steps` scrubbed split + combine steps with HIP
+    events on `stream`. Returns (split_ms, combine_ms, step_ms, wall_s)."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        evict()
+        split()
+        combine()
+    torch.cuda.synchronize()
+    note("warmup done; timing")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for k in range(steps):
+        evict()
+        evs[k][0].record(stream)
+        split()
+        evs[k][1].record(stream)
+        combine()
+        evs[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    return split_ms, comb_ms, step_ms, wall
+
+
+def variant_e5m2(cfg: int, dev, evict, steps: int, warmup: int) -> dict:
+    """The same workload stored as E5M2 bytes (the alternative KV format):
+    step and split-kernel times, measured like the main line."""
+    import torch
+
+    import paged_fp8_split_amd as pfs
+    from paged_fp8_split_amd import _lib
+    from paged_fp8_split_amd import workloads as W
+
+    note("generating the E5M2 variant of the workload")
+    w = W.config(cfg, kv_format="e5m2")
+    t = W.device_tensors(w, dev)
+    plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
+                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"], kv_format="e5m2")
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream(dev)
+    split = lambda: _lib.verify_split(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["block_table"],
+                                      t["live_len"], ws, stream)
+    combine = lambda: _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
+    split_ms, comb_ms, step_ms, _ = time_steps(split, combine, evict, stream, steps, warmup)
+    sb = split_algorithmic_bytes(w, plan)
+    ach = sb / (float(split_ms.mean()) * 1e-3) / 1e9
+    res = {
+        "workload": w.name + "-e5m2",
+        "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
+        "kv_GBps": round(w.kv_bytes() / (float(step_ms.mean()) * 1e-3) / 1e9, 2),
+        "split_mean_launch_us": round(float(split_ms.mean()) * 1e3, 2),
+        "split_achieved_GBps": round(ach, 2),
+        "split_frac": round(ach / PEAK_HBM_GBS, 4),
+        "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
+    }
+    del t, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, seconds: float) -> dict:
     """The FP64 oracle, as it stands, on the host cores: whole verify steps of
     the same workload, repeated until `seconds` have elapsed (at least one)."""
@@ -120,6 +247,7 @@ def main() -> int:
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the E5M2-format variant of the workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (to scale HBM byte counters) and exit")
     args = ap.parse_args()
@@ -173,28 +301,7 @@ def main() -> int:
         _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
 
     note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B")
-    for _ in range(args.warmup):
-        evict()
-        split()
-        combine()
-    torch.cuda.synchronize()
-    note("warmup done; timing")
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for k in range(args.steps):
-        evict()
-        evs[k][0].record(stream)
-        split()
-        evs[k][1].record(stream)
-        combine()
-        evs[k][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    split_ms, comb_ms, step_ms, wall = time_steps(split, combine, evict, stream, args.steps, args.warmup)
     y = out.cpu().numpy()
     out_sha = hashlib.sha256(y.tobytes()).hexdigest()
 
@@ -272,6 +379,11 @@ def main() -> int:
         "output_sha256": out_sha,
         "kernel_source_sha": kernel_source_sha(),
     }
+    note("timing the codec kernels")
+    res["codec"] = codec_timing(w, t, dev, evict)
+    if not args.no_variants:
+        res["variants"] = {"e5m2": variant_e5m2(args.config, dev, evict, max(args.steps // 2, 10),
+                                                 max(args.warmup // 2, 3))}
     if not args.no_cpu_baseline:
         note("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -9,9 +9,9 @@
  *   For request b, query head h (KV head g = head_map[h]) and draft row i in
  *   [0, q): the row attends causally to the first n_i = clamp(L_b - q + i + 1,
  *   0, L_b) tokens of the request's paged KV cache, where L_b = live_len[b]
- *   counts the q draft tokens. K and V are stored as OCP E4M3 (FN) bytes with
- *   one FP32 scale per KV head:  Khat = e4m3(k_byte) * k_scale[g],
- *   Vhat = e4m3(v_byte) * v_scale[g].
+ *   counts the q draft tokens. K and V are stored as OCP E4M3 (FN) bytes
+ *   (or, on request, E5M2 bytes: PFS_KV_E5M2) with one FP32 scale per KV
+ *   head:  Khat = dec(k_byte) * k_scale[g],  Vhat = dec(v_byte) * v_scale[g].
  *     s_j  = sm_scale * dot(Q[b,i,h,:], Khat_j)          for j < n_i
  *     out  = sum_j exp(s_j - max s) Vhat_j / sum_j exp(s_j - max s)
  *   rounded once to FP16 (round to nearest even). A row with n_i == 0
@@ -45,7 +45,7 @@ extern "C" {
  * changes. Callers refuse a library whose pfs_abi_version() differs from the
  * header they were built against (the pages' "stale native rejection":
  * "[Bugfix] Use FP32 state ...", Purpose, precision revision / rebuild). */
-#define PFS_ABI_VERSION 2
+#define PFS_ABI_VERSION 3
 
 enum {
     PFS_OK = 0,
@@ -58,6 +58,18 @@ enum {
     PFS_ERR_LAUNCH = -7,      /* the HIP runtime reported an error at launch */
     PFS_ERR_NOMEM = -8        /* host allocation of the plan failed */
 };
+
+/* How the bytes of the KV pools encode values (pfs_problem.kv_format).
+ * E4M3 is the method's format: OCP E4M3FN, bias 7, largest finite 448, no
+ * infinities, S.1111.111 = NaN. E5M2 is the explicit alternative the pages
+ * keep beside it ("[Bugfix] Use FP32 state and E4M3 defaults for DFlash2",
+ * Purpose: E4M3 by default, E5M2 on request; "[Kernel][SM70] Add opt-in
+ * E4M3 grouped attention with FP32 partials", historical scope: explicit
+ * E5M2 routes kept): bias 15, largest finite 57344, S.11111.00 = infinity,
+ * S.11111.xx (xx != 0) = NaN; every E5M2 value is the FP16 number whose high
+ * byte it is. Only the decoder (and the quantize-on-write encoder) differs;
+ * scales, layout and the rest of the arithmetic are the same. */
+enum { PFS_KV_E4M3 = 0, PFS_KV_E5M2 = 1 };
 
 /* Opaque HIP stream handle (hipStream_t); NULL is the default stream. */
 typedef struct ihipStream_t* pfs_stream_t;
@@ -90,6 +102,7 @@ typedef struct pfs_problem {
     int32_t num_pool_pages;     /* physical pages in each pool */
     int32_t partition_tokens;   /* 64 (the only partition size this build runs) */
     int32_t tokens_per_split;   /* 0 = library default; else a multiple of partition_tokens */
+    int32_t kv_format;          /* PFS_KV_E4M3 (0) or PFS_KV_E5M2 (1): how the pool bytes decode */
     int64_t kv_page_stride;     /* bytes, multiple of 16 */
     int64_t kv_token_stride;    /* bytes, multiple of 16 */
     int64_t kv_head_stride;     /* bytes, multiple of 16, >= head_dim */
@@ -142,8 +155,9 @@ int32_t pfs_plan_tokens_per_split(const pfs_plan* plan);
  * Device-side preconditions (not checked on the host, which must not
  * synchronize): live_len values are clamped into [0, capacity]; block-table
  * entries are read only for logical pages below ceil(L_b / page_size) and
- * must lie in [0, num_pool_pages); live K/V bytes are finite E4M3 codes
- * (bytes no live token owns may hold anything, NaN codes included).
+ * must lie in [0, num_pool_pages); live K/V bytes are finite codes of the
+ * plan's KV format (bytes no live token owns may hold anything, NaN and
+ * infinity codes included).
  * All buffers are caller-owned. Returns PFS_OK or an error status; a launch
  * error is reported as PFS_ERR_LAUNCH.
  */
@@ -170,18 +184,19 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
                            pfs_stream_t stream);
 
 /*
- * E4M3 paged -> FP16 bridge (the dequant-on-load path exposed on its own;
+ * Paged FP8 -> FP16 bridge (the dequant-on-load path exposed on its own;
  * "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
  * Scope list: an explicit E4M3 paged-to-FP16 bridge API).
  * Writes out_fp16 as a dense device array [batch, capacity, num_kv_heads,
  * head_dim] (capacity = max_pages_per_row * page_size): element (b, t, g, d)
- * is e4m3(byte) * scale[g] rounded once to the nearest FP16 (ties to even)
- * for the pool byte of token t of request b when t < live_len[b], and +0.0
- * otherwise. scale is a device [num_kv_heads] FP32 array, or NULL for the
- * unscaled decode (exact: every finite E4M3 value is an FP16 number). NaN
- * codes give NaN. Same alignment and precondition rules as pfs_verify; no
- * workspace. Only the plan's batch, num_kv_heads, head_dim, page size,
- * max_pages_per_row and strides are used.
+ * is dec(byte) * scale[g] rounded once to the nearest FP16 (ties to even),
+ * dec being the plan's KV format decoder, for the pool byte of token t of
+ * request b when t < live_len[b], and +0.0 otherwise. scale is a device
+ * [num_kv_heads] FP32 array, or NULL for the unscaled decode (exact: every
+ * E4M3 and E5M2 value is an FP16 number). NaN codes give NaN, E5M2
+ * infinities give infinities. Same alignment and precondition rules as
+ * pfs_verify; no workspace. Only the plan's batch, num_kv_heads, head_dim,
+ * page size, max_pages_per_row, strides and KV format are used.
  */
 int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float* scale,
                           const int32_t* block_table, const int32_t* live_len, void* out_fp16,
@@ -198,14 +213,16 @@ int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float
  *                          draft tokens, row i being token live_len[b] - q + i
  *   k_scale/v_scale        device [num_kv_heads] FP32
  *   k_pool/v_pool          the plan's paged pools, written in place
- * Each value x is stored as the E4M3FN code nearest to the FP32 quotient
- * x / scale (IEEE single division), ties to even, saturating at +-448
- * (infinities included); a NaN quotient stores 0x7F. Rows that would land
+ * Each value x is stored as the code of the plan's KV format nearest to
+ * the FP32 quotient x / scale (IEEE single division), ties to even,
+ * saturating at the largest finite value (+-448 for E4M3, +-57344 for E5M2;
+ * infinities included); a NaN quotient stores 0x7F (NaN in both formats).
+ * Rows that would land
  * before token 0 (live_len[b] < q) are not written; no other byte of the
  * pools changes. Lengths are clamped into [0, capacity]; block-table entries
  * of the written tokens must lie in [0, num_pool_pages) (not checked on the
- * host). Uses the plan's batch, q, num_kv_heads, head_dim, page size and
- * strides. Enqueue only, no allocation; capturable.
+ * host). Uses the plan's batch, q, num_kv_heads, head_dim, page size,
+ * strides and KV format. Enqueue only, no allocation; capturable.
  */
 int32_t pfs_kv_append(const pfs_plan* plan, const void* k_new_fp16, const void* v_new_fp16,
                       const float* k_scale, const float* v_scale, const int32_t* block_table,

@@ -12,7 +12,7 @@ from __future__ import annotations
 import math
 from typing import Dict, Optional, Sequence, Tuple
 
-__all__ = ["verify", "dequant_paged", "kv_append", "make_plan", "Plan", "PfsError", "ABI_VERSION"]
+__all__ = ["verify", "dequant_paged", "kv_append", "make_plan", "Plan", "PfsError", "ABI_VERSION", "KV_FORMATS"]
 
 _plans: Dict[Tuple, "Plan"] = {}
 
@@ -25,6 +25,24 @@ def __getattr__(name):
     raise AttributeError(name)
 
 
+KV_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _kv_format(pool, kv_format: Optional[str]) -> int:
+    """PFS_KV_* code of a pool: the explicit ``kv_format`` ("e4m3" or "e5m2"),
+    else the pool's float8 dtype, else E4M3 (uint8 pools)."""
+    import torch
+
+    implied = {torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}.get(pool.dtype)
+    if kv_format is None:
+        kv_format = implied or "e4m3"
+    if kv_format not in KV_FORMATS:
+        raise ValueError(f"kv_format must be one of {sorted(KV_FORMATS)}, got {kv_format!r}")
+    if implied is not None and implied != kv_format:
+        raise ValueError(f"kv_format {kv_format!r} contradicts the pool dtype {pool.dtype}")
+    return KV_FORMATS[kv_format]
+
+
 def _pool_layout(pool):
     if pool.dtype.itemsize != 1 or pool.dim() != 4:
         raise ValueError("KV pools must be uint8 tensors shaped [pages, page_size, kv_heads, head_dim]")
@@ -35,34 +53,38 @@ def _pool_layout(pool):
 
 
 def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_scale=None,
-              partition_tokens=64, tokens_per_split=0):
+              partition_tokens=64, tokens_per_split=0, kv_format: Optional[str] = None):
     """Plan (cached) for a problem whose KV pools look like ``k_pool``."""
     from . import _lib
 
     pages, page, hkv, d, (sp, st, sh) = _pool_layout(k_pool)
+    fmt = _kv_format(k_pool, kv_format)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     hm = tuple(int(x) for x in head_map)
     key = (batch, q, num_q_heads, hkv, d, page, max_pages_per_row, pages, sp, st, sh, float(sm_scale), hm,
-           partition_tokens, tokens_per_split)
+           partition_tokens, tokens_per_split, fmt)
     plan = _plans.get(key)
     if plan is None:
         plan = _lib.Plan(batch=batch, q=q, num_q_heads=num_q_heads, num_kv_heads=hkv, head_dim=d, page_size=page,
                          max_pages_per_row=max_pages_per_row, num_pool_pages=pages, kv_page_stride=sp,
                          kv_token_stride=st, kv_head_stride=sh, sm_scale=sm_scale, head_map=hm,
-                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split)
+                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split, kv_format=fmt)
         _plans[key] = plan
     return plan
 
 
 def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_map: Optional[Sequence[int]] = None,
            sm_scale: Optional[float] = None, partition_tokens: int = 64, tokens_per_split: int = 0, out=None,
-           workspace=None, stream=None, plan=None):
-    """Verify attention of q draft rows per request over a paged E4M3 KV cache.
+           workspace=None, stream=None, plan=None, kv_format: Optional[str] = None):
+    """Verify attention of q draft rows per request over a paged FP8 KV cache.
 
     q            [B, q, Hq, D] float16, contiguous, on the GPU
-    k_pool/v_pool [pages, page_size, Hkv, D] uint8 (E4M3 bytes), head_dim
-                 contiguous, identical strides (multiples of 16 bytes)
+    k_pool/v_pool [pages, page_size, Hkv, D] byte tensors (uint8 or a float8
+                 dtype), head_dim contiguous, identical strides (multiples of
+                 16 bytes)
+    kv_format    "e4m3" (default) or "e5m2"; a float8_e4m3fn / float8_e5m2
+                 pool dtype implies it
     k_scale/v_scale [Hkv] float32
     block_table  [B, max_pages_per_row] int32
     live_len     [B] int32, draft tokens included
@@ -83,7 +105,12 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     if plan is None:
         plan = make_plan(batch=B, q=nq, num_q_heads=Hq, head_map=head_map, k_pool=k_pool,
                          max_pages_per_row=int(block_table.shape[1]), sm_scale=sm_scale,
-                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split)
+                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split,
+                         kv_format=kv_format)
+    elif plan.kv_format != _kv_format(k_pool, kv_format):
+        raise ValueError("the plan's KV format differs from the pools'")
+    if v_pool.dtype != k_pool.dtype:
+        raise ValueError("K and V pools must share a dtype")
     for name, t, dt in (("k_scale", k_scale, torch.float32), ("v_scale", v_scale, torch.float32),
                         ("block_table", block_table, torch.int32), ("live_len", live_len, torch.int32)):
         if t.dtype != dt or not t.is_contiguous():
@@ -96,10 +123,12 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     return out
 
 
-def dequant_paged(pool, block_table, live_len, *, scale=None, out=None, stream=None):
-    """Paged E4M3 pool -> dense float16 [B, capacity, Hkv, D]: each byte's
-    value times ``scale`` (float32 [Hkv], optional) rounded once to FP16;
-    tokens at or beyond a request's live length are +0.0."""
+def dequant_paged(pool, block_table, live_len, *, scale=None, out=None, stream=None,
+                  kv_format: Optional[str] = None):
+    """Paged FP8 pool -> dense float16 [B, capacity, Hkv, D]: each byte's
+    value (E4M3 or E5M2, as for ``verify``) times ``scale`` (float32 [Hkv],
+    optional) rounded once to FP16; tokens at or beyond a request's live
+    length are +0.0."""
     from . import _lib
     import torch
 
@@ -108,18 +137,20 @@ def dequant_paged(pool, block_table, live_len, *, scale=None, out=None, stream=N
     if scale is not None and (scale.dtype != torch.float32 or not scale.is_contiguous() or scale.numel() != hkv):
         raise ValueError("scale must be a contiguous float32 tensor [num_kv_heads]")
     plan = make_plan(batch=B, q=1, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=pool,
-                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0)
+                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0, kv_format=kv_format)
     if out is None:
         out = torch.empty((B, plan.capacity, hkv, d), dtype=torch.float16, device=pool.device)
     _lib.dequant_paged(plan, pool, block_table, live_len, out, stream, scale=scale)
     return out
 
 
-def kv_append(k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, *, stream=None):
+def kv_append(k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, *, stream=None,
+              kv_format: Optional[str] = None):
     """Quantize-on-write: store the FP16 K/V [B, q, Hkv, D] of every request's
-    q draft tokens (row i at token live_len[b] - q + i) into the paged E4M3
-    pools, in place: the code nearest to x / scale, ties to even, saturating
-    at +-448. No host synchronization."""
+    q draft tokens (row i at token live_len[b] - q + i) into the paged FP8
+    pools (E4M3 or E5M2, as for ``verify``), in place: the code nearest to
+    x / scale, ties to even, saturating at the largest finite value (448 or
+    57344). No host synchronization."""
     from . import _lib
     import torch
 
@@ -132,6 +163,8 @@ def kv_append(k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_p
     pages, page, phkv, pd, _ = _pool_layout(k_pool)
     if (phkv, pd) != (hkv, d):
         raise ValueError("k_new and the pools disagree on num_kv_heads / head_dim")
+    if v_pool.dtype != k_pool.dtype:
+        raise ValueError("K and V pools must share a dtype")
     plan = make_plan(batch=B, q=nq, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=k_pool,
-                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0)
+                     max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0, kv_format=kv_format)
     _lib.kv_append(plan, k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, stream)

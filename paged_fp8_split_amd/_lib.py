@@ -60,6 +60,7 @@ class PfsProblem(ctypes.Structure):
         ("num_pool_pages", ctypes.c_int32),
         ("partition_tokens", ctypes.c_int32),
         ("tokens_per_split", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
         ("kv_page_stride", ctypes.c_int64),
         ("kv_token_stride", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64),
@@ -128,14 +129,14 @@ class Plan:
 
     def __init__(self, *, batch, q, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_row,
                  num_pool_pages, kv_page_stride, kv_token_stride, kv_head_stride, sm_scale, head_map,
-                 partition_tokens=64, tokens_per_split=0):
+                 partition_tokens=64, tokens_per_split=0, kv_format=0):
         lib = load()
         self._lib = lib
         self._handle = None
         hm = (ctypes.c_int32 * int(num_q_heads))(*[int(x) for x in head_map])
         self.problem = PfsProblem(int(batch), int(q), int(num_q_heads), int(num_kv_heads), int(head_dim),
                                   int(page_size), int(max_pages_per_row), int(num_pool_pages),
-                                  int(partition_tokens), int(tokens_per_split), int(kv_page_stride),
+                                  int(partition_tokens), int(tokens_per_split), int(kv_format), int(kv_page_stride),
                                   int(kv_token_stride), int(kv_head_stride), float(sm_scale),
                                   ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32)))
         handle = ctypes.c_void_p()
@@ -147,6 +148,7 @@ class Plan:
         self.num_splits = int(lib.pfs_plan_num_splits(handle))
         self.tokens_per_split = int(lib.pfs_plan_tokens_per_split(handle))
         self.capacity = int(max_pages_per_row) * int(page_size)
+        self.kv_format = int(kv_format)
 
     @property
     def handle(self):
@@ -200,7 +202,7 @@ def verify_combine(plan: Plan, v_scale, live_len, out, workspace, stream=None) -
 
 
 def dequant_paged(plan: Plan, pool, block_table, live_len, out, stream=None, scale=None) -> None:
-    """pfs_dequant_paged: paged E4M3 -> dense FP16 [B, capacity, Hkv, D],
+    """pfs_dequant_paged: paged FP8 (the plan's KV format) -> dense FP16 [B, capacity, Hkv, D],
     times ``scale`` [Hkv] (float32 tensor) rounded once, or unscaled."""
     st = plan._lib.pfs_dequant_paged(plan.handle, _ptr(pool), None if scale is None else _ptr(scale),
                                      _ptr(block_table), _ptr(live_len), _ptr(out), _stream_handle(pool.device, stream))
@@ -210,7 +212,7 @@ def dequant_paged(plan: Plan, pool, block_table, live_len, out, stream=None, sca
 
 def kv_append(plan: Plan, k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool,
               stream=None) -> None:
-    """pfs_kv_append: the draft tokens' FP16 K/V [B, q, Hkv, D] -> E4M3 bytes in the pools."""
+    """pfs_kv_append: the draft tokens' FP16 K/V [B, q, Hkv, D] -> FP8 bytes (the plan's KV format) in the pools."""
     st = plan._lib.pfs_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(block_table), _ptr(live_len), _ptr(k_pool), _ptr(v_pool),
                                  _stream_handle(k_pool.device, stream))

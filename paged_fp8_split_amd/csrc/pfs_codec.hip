@@ -1,28 +1,35 @@
 // pfs_codec.hip -- gfx950 kernels at the two ends of the paged E4M3 KV cache.
 //
 //   pfs_append_kernel   quantize-on-write: the FP16 K/V of every request's q
-//                       draft tokens -> E4M3 bytes in the paged pools (the
+//                       draft tokens -> FP8 bytes in the paged pools (the
 //                       step before verify: "[Kernel] Preserve DFlash2
 //                       sampling precision and repair QUASAR TP2", Purpose,
 //                       deferred accepted-slot writes; "[Bugfix] Use FP32
 //                       state and E4M3 defaults for DFlash2", Test Plan, KV
 //                       scaling)
-//   pfs_bridge_kernel   paged E4M3 -> dense FP16, optionally scaled
+//   pfs_bridge_kernel   paged FP8 -> dense FP16, optionally scaled
 //                       ("[Kernel][SM70] Add opt-in E4M3 grouped attention
 //                       with FP32 partials", Scope list: the explicit E4M3
 //                       paged-to-FP16 bridge API)
 //
-// Encoding: the stored byte is the E4M3FN code nearest to the FP32 quotient
-// x / scale (IEEE single division), ties to even, saturating at +-448 (the
-// quotient is clamped first, so infinities saturate too); a NaN quotient
-// stores 0x7F. The hardware conversion v_cvt_pk_fp8_f32 rounds to nearest
-// even on gfx950's OCP E4M3 format.
+// Both kernels exist for the two KV formats (template parameter FMT): OCP
+// E4M3FN, the method's format, and E5M2, the explicit alternative ("[Bugfix]
+// Use FP32 state and E4M3 defaults for DFlash2", Purpose).
 //
-// Bridge: e4m3(byte) * scale has up to 28 significant bits, so the FP32
+// Encoding: the stored byte is the code nearest to the FP32 quotient
+// x / scale (IEEE single division), ties to even, saturating at the largest
+// finite value (448 for E4M3, 57344 for E5M2: the quotient is clamped first,
+// so infinities saturate too); a NaN quotient stores 0x7F, a NaN code of
+// both formats. The hardware conversions v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32
+// round to nearest even.
+//
+// Bridge: dec(byte) * scale has up to 28 significant bits, so the FP32
 // product can be inexact; the kernel rounds it to odd in FP32 (product plus
 // its exact FMA error term) and then once to FP16, which equals one
 // round-to-nearest-even of the exact product (FP32 keeps more than two bits
-// beyond FP16's). Without a scale the decode is exact.
+// beyond FP16's). Without a scale the decode is exact: E4M3 through the
+// hardware conversion, E5M2 by placing each byte above a zero byte (an E5M2
+// byte is the high byte of its FP16 value).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,18 +44,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int32_t clamp_len(int32_t v, int32_t hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
 
-// E4M3 code of x / s for one FP32 value pair (a in the low byte).
+// Code of x / s for one FP32 value pair (x0 in the low byte).
+template <int FMT>
 __device__ __forceinline__ uint32_t encode2(float x0, float x1, float s) {
+    constexpr float kMax = FMT == PFS_KV_E5M2 ? 57344.0f : 448.0f;
     const float q0 = x0 / s, q1 = x1 / s;
-    const float c0 = fminf(fmaxf(q0, -448.0f), 448.0f);
-    const float c1 = fminf(fmaxf(q1, -448.0f), 448.0f);
-    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
+    const float c0 = fminf(fmaxf(q0, -kMax), kMax);
+    const float c1 = fminf(fmaxf(q1, -kMax), kMax);
+    uint32_t w;
+    if constexpr (FMT == PFS_KV_E5M2)
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false) & 0xFFFFu;
+    else
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
     if (q0 != q0) w = (w & 0xFF00u) | 0x7Fu;
     if (q1 != q1) w = (w & 0x00FFu) | 0x7F00u;
     return w;
 }
 
-// 8 FP16 values (one 16-byte word) -> 8 E4M3 bytes (two dwords).
+// 8 FP16 values (one 16-byte word) -> 8 code bytes (two dwords).
+template <int FMT>
 __device__ __forceinline__ u32x2 encode8(u32x4 h, float s) {
     u32x2 r;
     const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
@@ -56,7 +70,7 @@ __device__ __forceinline__ u32x2 encode8(u32x4 h, float s) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const f16x2 v = __builtin_bit_cast(f16x2, hw[k]);
-        b[k] = encode2((float)v.x, (float)v.y, s);
+        b[k] = encode2<FMT>((float)v.x, (float)v.y, s);
     }
     r.x = b[0] | (b[1] << 16);
     r.y = b[2] | (b[3] << 16);
@@ -86,6 +100,7 @@ struct AppendArgs {
 
 // One thread per 8 elements (one FP16 word) of one (request, draft row, KV
 // head): reads K and V, writes 8 bytes into each pool.
+template <int FMT>
 __global__ __launch_bounds__(256) void pfs_append_kernel(const AppendArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= a.words) return;
@@ -101,11 +116,12 @@ __global__ __launch_bounds__(256) void pfs_append_kernel(const AppendArgs a) {
     const int32_t page = a.block_table[(int64_t)b * a.max_pages + t / a.page_size];
     const int64_t off = (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride +
                         (int64_t)g * a.head_stride + 8 * c;
-    *reinterpret_cast<u32x2*>(a.k_pool + off) = encode8(a.k_new[idx], a.k_scale[g]);
-    *reinterpret_cast<u32x2*>(a.v_pool + off) = encode8(a.v_new[idx], a.v_scale[g]);
+    *reinterpret_cast<u32x2*>(a.k_pool + off) = encode8<FMT>(a.k_new[idx], a.k_scale[g]);
+    *reinterpret_cast<u32x2*>(a.v_pool + off) = encode8<FMT>(a.v_new[idx], a.v_scale[g]);
 }
 
-// FP16 of e4m3 * s, rounded once: round the FP32 product to odd, then to FP16.
+// FP16 of v * s (v an exactly decoded byte), rounded once: round the FP32
+// product to odd, then to FP16.
 __device__ __forceinline__ _Float16 scaled_half(float v, float s) {
     const float p = v * s;
     if (p == 0.0f || !isfinite(p)) return (_Float16)p;
@@ -134,7 +150,17 @@ struct BridgeArgs {
     int32_t capacity;
 };
 
+// Exact FP16 of two code bytes (bytes 2*HI and 2*HI+1 of `w`).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t decode2(uint32_t w) {
+    if constexpr (FMT == PFS_KV_E5M2)
+        return __builtin_amdgcn_perm(w, w, HI ? 0x030C020Cu : 0x010C000Cu);
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
 // One thread per 16 bytes of one (token, KV head); blockIdx.y is the request.
+template <int FMT>
 __global__ __launch_bounds__(256) void pfs_bridge_kernel(const BridgeArgs a) {
     const int chunks = a.head_dim / 16;
     const int64_t per_tok = (int64_t)a.num_kv_heads * chunks;
@@ -155,9 +181,9 @@ __global__ __launch_bounds__(256) void pfs_bridge_kernel(const BridgeArgs a) {
         uint32_t h[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            // exact FP16 decode of two bytes each (every finite E4M3 value is an FP16 number)
-            h[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[k], 1.0f, false));
-            h[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[k], 1.0f, true));
+            // exact FP16 decode of two bytes each (every E4M3 and E5M2 value is an FP16 number)
+            h[2 * k] = decode2<FMT, false>(ws[k]);
+            h[2 * k + 1] = decode2<FMT, true>(ws[k]);
         }
         if (a.scale) {
             const float s = a.scale[g];
@@ -203,8 +229,11 @@ int32_t pfs_launch_append(const pfs_plan* plan, const void* k_new, const void* v
     a.capacity = plan->capacity;
     a.words = (int64_t)p.batch * p.q * p.num_kv_heads * (p.head_dim / 8);
     const int64_t blocks = (a.words + 255) / 256;
-    hipLaunchKernelGGL(pfs_append_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                       a);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.kv_format == PFS_KV_E5M2)
+        hipLaunchKernelGGL(pfs_append_kernel<PFS_KV_E5M2>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(pfs_append_kernel<PFS_KV_E4M3>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
 
@@ -227,6 +256,10 @@ int32_t pfs_launch_bridge(const pfs_plan* plan, const uint8_t* pool, const float
     a.capacity = plan->capacity;
     const int64_t threads = (int64_t)plan->capacity * p.num_kv_heads * (p.head_dim / 16);
     const dim3 grid((unsigned)((threads + 255) / 256), p.batch);
-    hipLaunchKernelGGL(pfs_bridge_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.kv_format == PFS_KV_E5M2)
+        hipLaunchKernelGGL(pfs_bridge_kernel<PFS_KV_E5M2>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(pfs_bridge_kernel<PFS_KV_E4M3>, grid, dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }

@@ -1,7 +1,11 @@
 // pfs_kernels.hip -- gfx950 (CDNA4) kernels of libpfs and their launchers.
 //
-//   e4m3x2_to_f16x2       exact E4M3 -> FP16 dequant-on-load (hardware
-//                         v_cvt_scalef32_pk_f16_fp8 with scale 1.0)
+//   fp8x2_to_f16x2        exact FP8 -> FP16 dequant-on-load: E4M3 through
+//                         the hardware v_cvt_scalef32_pk_f16_fp8 (scale 1.0),
+//                         E5M2 (the explicitly requested alternative KV
+//                         format: "[Bugfix] Use FP32 state and E4M3 defaults
+//                         for DFlash2", Purpose) by a byte permute, an E5M2
+//                         byte being the high byte of its FP16 value
 //   pfs_split_kernel      per-split QK^T (MFMA), online softmax, PV (MFMA);
 //                         emits FP32 (max, sum, unnormalized PV) per split
 //   pfs_combine_kernel    rescales the splits, sums them in a fixed order
@@ -50,8 +54,8 @@
 // against a lazily raised reference maximum m_ref; the row sums come from the
 // matrix core (a ones row times the same FP16 P the PV product uses); V's
 // scale is applied once in the combine. Masked scores are selected to -inf and
-// K/V bytes beyond the live length are never loaded (zero), so NaN tail bytes
-// cannot leak.
+// K/V bytes beyond the live length are never loaded (zero), so NaN (or E5M2
+// infinity) tail bytes cannot leak.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -79,21 +83,29 @@ __device__ __forceinline__ T bit_cast_(F f) {
     return __builtin_bit_cast(T, f);
 }
 
-// Two E4M3 bytes (bytes 2*HI and 2*HI+1 of `word`) -> two FP16 values, exact:
-// every finite E4M3 value is zero or an FP16 normal number.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t word) {
-    const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, HI);
-    return bit_cast_<uint32_t>(h);
+// Two KV bytes (bytes 2*HI and 2*HI+1 of `word`) -> two FP16 values, exact.
+// E4M3: every finite value is zero or an FP16 normal number; the hardware
+// conversion decodes it. E5M2: a byte is the high byte of the FP16 number it
+// encodes (same exponent width and bias), so one byte permute places both
+// bytes above zero low bytes (selector 0x0C yields a zero byte).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t word) {
+    if constexpr (FMT == PFS_KV_E5M2) {
+        return __builtin_amdgcn_perm(word, word, HI ? 0x030C020Cu : 0x010C000Cu);
+    } else {
+        const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, HI);
+        return bit_cast_<uint32_t>(h);
+    }
 }
 
-// 8 E4M3 bytes (two dwords) -> 8 FP16 values as an MFMA operand.
-__device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
+// 8 KV bytes (two dwords) -> 8 FP16 values as an MFMA operand.
+template <int FMT>
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
     u32x4 r;
-    r.x = e4m3x2_to_f16x2<false>(w0);
-    r.y = e4m3x2_to_f16x2<true>(w0);
-    r.z = e4m3x2_to_f16x2<false>(w1);
-    r.w = e4m3x2_to_f16x2<true>(w1);
+    r.x = fp8x2_to_f16x2<FMT, false>(w0);
+    r.y = fp8x2_to_f16x2<FMT, true>(w0);
+    r.z = fp8x2_to_f16x2<FMT, false>(w1);
+    r.w = fp8x2_to_f16x2<FMT, true>(w1);
     return bit_cast_<f16x8>(r);
 }
 
@@ -216,7 +228,7 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
 // transposed read get distinct values, so the block hits distinct banks.
 __device__ __forceinline__ int v_swizzle(int t, int swb) { return ((t & 3) | ((t >> 4) << 2)) & (swb - 1); }
 
-template <int D, int RT, int RG, int TP, int NS>
+template <int D, int RT, int RG, int TP, int NS, int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * RG * TP, 64 * RG * TP),
                           amdgpu_waves_per_eu(SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU,
                                               SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU))) void
@@ -480,8 +492,8 @@ pfs_split_kernel(const SplitArgs a) {
     auto qk_fold = [&](const KChunk& kc, int j, Scores& sc) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const f16x8 k_lo = e4m3x8_to_f16x8(kc.w[mt].x, kc.w[mt].y);
-            const f16x8 k_hi = e4m3x8_to_f16x8(kc.w[mt].z, kc.w[mt].w);
+            const f16x8 k_lo = fp8x8_to_f16x8<FMT>(kc.w[mt].x, kc.w[mt].y);
+            const f16x8 k_hi = fp8x8_to_f16x8<FMT>(kc.w[mt].z, kc.w[mt].w);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) {
                 sc.v[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, qop[nt][2 * j], sc.v[mt][nt], 0, 0, 0);
@@ -565,7 +577,7 @@ pfs_split_kernel(const SplitArgs a) {
     auto pv_fold = [&](const VChunk& vc, int md0, const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f16x8 vop = e4m3x8_to_f16x8((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
+            const f16x8 vop = fp8x8_to_f16x8<FMT>((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
                 acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md0 + u][nt], 0, 0, 0);
@@ -870,38 +882,50 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const Comb
 }
 
 
-template <int D, int RT, int RG>
+template <int D, int RT, int RG, int FMT>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
     constexpr int W = pfs::split_waves(D, RG);
     constexpr int TP = W / RG;
     constexpr int NS = pfs::split_stages(D, TP, W);
     const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
     const int64_t wgs = ((units + 7) / 8) * 8 * a.row_blocks;
-    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS>), dim3((unsigned)wgs), dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS, FMT>), dim3((unsigned)wgs), dim3(64 * W), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
 // Row groups above one occur only with the most row tiles a wave can hold.
-template <int D, int RT>
+template <int D, int RT, int FMT>
 hipError_t launch_split_rt(const SplitArgs& a, int32_t row_groups, hipStream_t stream) {
     if constexpr (RT > pfs::max_row_tiles(D)) {
         return hipErrorInvalidValue;
     } else {
-        if (row_groups == 1) return launch_split<D, RT, 1>(a, stream);
+        if (row_groups == 1) return launch_split<D, RT, 1, FMT>(a, stream);
         if constexpr (RT == pfs::max_row_tiles(D)) {
-            if (row_groups == 2) return launch_split<D, RT, 2>(a, stream);
-            if (row_groups == 4) return launch_split<D, RT, 4>(a, stream);
+            if (row_groups == 2) return launch_split<D, RT, 2, FMT>(a, stream);
+            if (row_groups == 4) return launch_split<D, RT, 4, FMT>(a, stream);
         }
         return hipErrorInvalidValue;
     }
 }
 
-template <int D>
+template <int D, int FMT>
 hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t row_groups, hipStream_t stream) {
     switch (row_tiles) {
-        case 1: return launch_split_rt<D, 1>(a, row_groups, stream);
-        case 2: return launch_split_rt<D, 2>(a, row_groups, stream);
-        case 4: return launch_split_rt<D, 4>(a, row_groups, stream);
+        case 1: return launch_split_rt<D, 1, FMT>(a, row_groups, stream);
+        case 2: return launch_split_rt<D, 2, FMT>(a, row_groups, stream);
+        case 4: return launch_split_rt<D, 4, FMT>(a, row_groups, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+hipError_t launch_split_fmt(const SplitArgs& a, int32_t head_dim, int32_t row_tiles, int32_t row_groups,
+                            hipStream_t stream) {
+    switch (head_dim) {
+        case 64: return launch_split_d<64, FMT>(a, row_tiles, row_groups, stream);
+        case 128: return launch_split_d<128, FMT>(a, row_tiles, row_groups, stream);
+        case 256: return launch_split_d<256, FMT>(a, row_tiles, row_groups, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -941,11 +965,11 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     for (int i = 0; i < pfs::kMaxQHeads; ++i) sa.qhead[i] = plan->qhead[i];
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256) return PFS_ERR_UNSUPPORTED;
     hipError_t e;
-    switch (p.head_dim) {
-        case 64: e = launch_split_d<64>(sa, plan->row_tiles, plan->row_groups, s); break;
-        case 128: e = launch_split_d<128>(sa, plan->row_tiles, plan->row_groups, s); break;
-        case 256: e = launch_split_d<256>(sa, plan->row_tiles, plan->row_groups, s); break;
+    switch (p.kv_format) {
+        case PFS_KV_E4M3: e = launch_split_fmt<PFS_KV_E4M3>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s); break;
+        case PFS_KV_E5M2: e = launch_split_fmt<PFS_KV_E5M2>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;

@@ -37,7 +37,7 @@ def run(w: W.Workload, *, tokens_per_split: int = 0, tensors=None, out=None, wor
     t = tensors if tensors is not None else W.device_tensors(w, dev)
     o = pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
                    head_map=t["head_map"], sm_scale=t["sm_scale"], tokens_per_split=tokens_per_split, out=out,
-                   workspace=workspace, stream=stream)
+                   workspace=workspace, stream=stream, kv_format=t.get("kv_format"))
     return o, t
 
 

@@ -84,6 +84,8 @@ def test_valid_problem_plans():
     (dict(q=17), "PFS_ERR_UNSUPPORTED"),
     (dict(page_size=40, kv_page_stride=40 * 512), "PFS_ERR_UNSUPPORTED"),
     (dict(partition_tokens=32), "PFS_ERR_UNSUPPORTED"),
+    (dict(kv_format=2), "PFS_ERR_UNSUPPORTED"),
+    (dict(kv_format=-1), "PFS_ERR_UNSUPPORTED"),
     (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
     (dict(num_q_heads=15, head_map=[0] * 15), "PFS_ERR_SHAPE"),
     (dict(batch=-1), "PFS_ERR_SHAPE"),
@@ -100,6 +102,14 @@ def test_valid_problem_plans():
 ])
 def test_invalid_problems_are_rejected(over, status):
     assert plan_status(**over) == _lib.STATUS_CODE[status]
+
+
+def test_both_kv_formats_plan_identically():
+    # the format changes only the decoder: same splits, same workspace
+    a, b = _lib.Plan(**BASE), _lib.Plan(**dict(BASE, kv_format=1))
+    assert (a.num_splits, a.tokens_per_split, a.workspace_bytes) == (b.num_splits, b.tokens_per_split,
+                                                                      b.workspace_bytes)
+    assert (a.kv_format, b.kv_format) == (0, 1)
 
 
 def test_head_major_pool_layout_is_accepted():
@@ -186,5 +196,5 @@ def test_plan_create_null_arguments():
     lib = _lib.load()
     h = ctypes.c_void_p()
     assert lib.pfs_plan_create(None, ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
-    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 64 * 512, 512, 256, 0.0625, None)
+    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 64 * 512, 512, 256, 0.0625, None)
     assert lib.pfs_plan_create(ctypes.byref(prob), ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
