@@ -172,20 +172,24 @@ def time_steps(split, combine, evict, stream, steps: int, warmup: int):
     return split_ms, comb_ms, step_ms, wall
 
 
-def variant_e5m2(cfg: int, dev, evict, steps: int, warmup: int) -> dict:
-    """The same workload stored as E5M2 bytes (the alternative KV format):
-    step and split-kernel times, measured like the main line."""
+def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3", pv_residual: bool = False,
+            w=None) -> dict:
+    """The workload in another mode of the path (E5M2 bytes, or high/residual
+    FP16 probabilities): step and split-kernel times, measured like the main
+    line."""
     import torch
 
     import paged_fp8_split_amd as pfs
     from paged_fp8_split_amd import _lib
     from paged_fp8_split_amd import workloads as W
 
-    note("generating the E5M2 variant of the workload")
-    w = W.config(cfg, kv_format="e5m2")
+    if w is None:
+        note(f"generating the {kv_format} workload")
+        w = W.config(cfg, kv_format=kv_format)
     t = W.device_tensors(w, dev)
     plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
-                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"], kv_format="e5m2")
+                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"], kv_format=kv_format,
+                         pv_residual=pv_residual)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
@@ -196,7 +200,7 @@ def variant_e5m2(cfg: int, dev, evict, steps: int, warmup: int) -> dict:
     sb = split_algorithmic_bytes(w, plan)
     ach = sb / (float(split_ms.mean()) * 1e-3) / 1e9
     res = {
-        "workload": w.name + "-e5m2",
+        "workload": w.name + ("-e5m2" if kv_format == "e5m2" else "") + ("-pv-residual" if pv_residual else ""),
         "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
         "kv_GBps": round(w.kv_bytes() / (float(step_ms.mean()) * 1e-3) / 1e9, 2),
         "split_mean_launch_us": round(float(split_ms.mean()) * 1e3, 2),
@@ -247,7 +251,8 @@ def main() -> int:
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-variants", action="store_true", help="skip the E5M2-format variant of the workload")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the residual-probability and E5M2 variants of the workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (to scale HBM byte counters) and exit")
     args = ap.parse_args()
@@ -382,8 +387,11 @@ def main() -> int:
     note("timing the codec kernels")
     res["codec"] = codec_timing(w, t, dev, evict)
     if not args.no_variants:
-        res["variants"] = {"e5m2": variant_e5m2(args.config, dev, evict, max(args.steps // 2, 10),
-                                                 max(args.warmup // 2, 3))}
+        vs, vw = max(args.steps // 2, 10), max(args.warmup // 2, 3)
+        res["variants"] = {
+            "pv_residual": variant(args.config, dev, evict, vs, vw, pv_residual=True, w=w),
+            "e5m2": variant(args.config, dev, evict, vs, vw, kv_format="e5m2"),
+        }
     if not args.no_cpu_baseline:
         note("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

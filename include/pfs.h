@@ -45,7 +45,7 @@ extern "C" {
  * changes. Callers refuse a library whose pfs_abi_version() differs from the
  * header they were built against (the pages' "stale native rejection":
  * "[Bugfix] Use FP32 state ...", Purpose, precision revision / rebuild). */
-#define PFS_ABI_VERSION 3
+#define PFS_ABI_VERSION 4
 
 enum {
     PFS_OK = 0,
@@ -70,6 +70,17 @@ enum {
  * byte it is. Only the decoder (and the quantize-on-write encoder) differs;
  * scales, layout and the rest of the arithmetic are the same. */
 enum { PFS_KV_E4M3 = 0, PFS_KV_E5M2 = 1 };
+
+/* High/residual probabilities (pfs_problem.pv_residual = 1; "[Kernel][SM70]
+ * Add opt-in E4M3 grouped attention with FP32 partials", historical scope:
+ * the PV probability as high/residual FP16 operands, the residual scaled by
+ * 2048 against an exactly representable inverse scale on E4M3-derived V).
+ * Each probability p (FP32) enters the PV product as hi = RNE_fp16(p) and
+ * res = RNE_fp16((p - hi) * 2048); the kernel adds hi * V + res * (V / 2048),
+ * where V / 2048 is exact in FP16 for every E4M3 value, and the row sums get
+ * hi + res / 2048 likewise. The FP16 rounding of P then costs about 2^-22
+ * instead of 2^-12 relative; the PV matrix work doubles. Not defined for
+ * E5M2 pools (V / 2048 is not exact there): PFS_ERR_UNSUPPORTED. */
 
 /* Opaque HIP stream handle (hipStream_t); NULL is the default stream. */
 typedef struct ihipStream_t* pfs_stream_t;
@@ -103,6 +114,8 @@ typedef struct pfs_problem {
     int32_t partition_tokens;   /* 64 (the only partition size this build runs) */
     int32_t tokens_per_split;   /* 0 = library default; else a multiple of partition_tokens */
     int32_t kv_format;          /* PFS_KV_E4M3 (0) or PFS_KV_E5M2 (1): how the pool bytes decode */
+    int32_t pv_residual;        /* 0: P enters PV as one FP16 operand; 1: as an FP16 high part
+                                   plus an FP16 residual (see below); E4M3 only */
     int64_t kv_page_stride;     /* bytes, multiple of 16 */
     int64_t kv_token_stride;    /* bytes, multiple of 16 */
     int64_t kv_head_stride;     /* bytes, multiple of 16, >= head_dim */

@@ -53,7 +53,8 @@ def _pool_layout(pool):
 
 
 def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_scale=None,
-              partition_tokens=64, tokens_per_split=0, kv_format: Optional[str] = None):
+              partition_tokens=64, tokens_per_split=0, kv_format: Optional[str] = None,
+              pv_residual: bool = False):
     """Plan (cached) for a problem whose KV pools look like ``k_pool``."""
     from . import _lib
 
@@ -63,20 +64,21 @@ def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_
         sm_scale = 1.0 / math.sqrt(d)
     hm = tuple(int(x) for x in head_map)
     key = (batch, q, num_q_heads, hkv, d, page, max_pages_per_row, pages, sp, st, sh, float(sm_scale), hm,
-           partition_tokens, tokens_per_split, fmt)
+           partition_tokens, tokens_per_split, fmt, bool(pv_residual))
     plan = _plans.get(key)
     if plan is None:
         plan = _lib.Plan(batch=batch, q=q, num_q_heads=num_q_heads, num_kv_heads=hkv, head_dim=d, page_size=page,
                          max_pages_per_row=max_pages_per_row, num_pool_pages=pages, kv_page_stride=sp,
                          kv_token_stride=st, kv_head_stride=sh, sm_scale=sm_scale, head_map=hm,
-                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split, kv_format=fmt)
+                         partition_tokens=partition_tokens, tokens_per_split=tokens_per_split, kv_format=fmt,
+                         pv_residual=int(bool(pv_residual)))
         _plans[key] = plan
     return plan
 
 
 def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_map: Optional[Sequence[int]] = None,
            sm_scale: Optional[float] = None, partition_tokens: int = 64, tokens_per_split: int = 0, out=None,
-           workspace=None, stream=None, plan=None, kv_format: Optional[str] = None):
+           workspace=None, stream=None, plan=None, kv_format: Optional[str] = None, pv_residual: bool = False):
     """Verify attention of q draft rows per request over a paged FP8 KV cache.
 
     q            [B, q, Hq, D] float16, contiguous, on the GPU
@@ -85,6 +87,8 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
                  16 bytes)
     kv_format    "e4m3" (default) or "e5m2"; a float8_e4m3fn / float8_e5m2
                  pool dtype implies it
+    pv_residual  carry each probability into PV as an FP16 high part plus an
+                 FP16 residual scaled by 2048 (E4M3 only; twice the PV work)
     k_scale/v_scale [Hkv] float32
     block_table  [B, max_pages_per_row] int32
     live_len     [B] int32, draft tokens included
@@ -106,7 +110,7 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
         plan = make_plan(batch=B, q=nq, num_q_heads=Hq, head_map=head_map, k_pool=k_pool,
                          max_pages_per_row=int(block_table.shape[1]), sm_scale=sm_scale,
                          partition_tokens=partition_tokens, tokens_per_split=tokens_per_split,
-                         kv_format=kv_format)
+                         kv_format=kv_format, pv_residual=pv_residual)
     elif plan.kv_format != _kv_format(k_pool, kv_format):
         raise ValueError("the plan's KV format differs from the pools'")
     if v_pool.dtype != k_pool.dtype:

@@ -109,6 +109,20 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
     return bit_cast_<f16x8>(r);
 }
 
+// 8 E4M3 bytes -> 8 FP16 values times 2^-11, exact: the smallest E4M3
+// magnitude, 2^-9, becomes 2^-20, a multiple of FP16's 2^-24 subnormal step,
+// and every E4M3 significand (4 bits) fits. The operand of the residual
+// probabilities (which carry a factor 2^11).
+__device__ __forceinline__ f16x8 e4m3x8_to_f16x8_res(uint32_t w0, uint32_t w1) {
+    constexpr float kInv = 1.0f / 2048.0f;
+    u32x4 r;
+    r.x = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, kInv, false));
+    r.y = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, kInv, true));
+    r.z = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, kInv, false));
+    r.w = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, kInv, true));
+    return bit_cast_<f16x8>(r);
+}
+
 // Max over the four lanes l, l^16, l^32, l^48 (the lane groups holding one
 // result column). v_permlane16/32_swap return both halves of a swap; the max
 // of the pair is the xor-16 / xor-32 butterfly step, identical in every lane.
@@ -228,7 +242,7 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
 // transposed read get distinct values, so the block hits distinct banks.
 __device__ __forceinline__ int v_swizzle(int t, int swb) { return ((t & 3) | ((t >> 4) << 2)) & (swb - 1); }
 
-template <int D, int RT, int RG, int TP, int NS, int FMT>
+template <int D, int RT, int RG, int TP, int NS, int FMT, bool RES>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * RG * TP, 64 * RG * TP),
                           amdgpu_waves_per_eu(SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU,
                                               SplitCfg<D, RT, RG, TP, NS>::WAVES_PER_EU))) void
@@ -357,6 +371,7 @@ pfs_split_kernel(const SplitArgs a) {
     const _Float16 one_or_zero = (lc == 0) ? (_Float16)1.0f : (_Float16)0.0f;
     const f16x8 ones = f16x8{one_or_zero, one_or_zero, one_or_zero, one_or_zero,
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
+    const f16x8 ones_res = ones * (_Float16)(1.0f / 2048.0f);  // row 0 = 2^-11, for the residual sums
 
     // transposed V reads: lane j of each 16-lane block names 8 bytes of token
     // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk. With
@@ -506,7 +521,14 @@ pfs_split_kernel(const SplitArgs a) {
     };
     // online softmax, log2 domain, lazy reference maximum. Scores are scaled
     // before masking, so a masked score is exactly -inf for any finite K scale.
-    auto softmax = [&](int32_t t_step, const Scores& sc, bool edge, f16x8 (&pop)[RT]) __attribute__((always_inline)) {
+    // The FP16 probabilities of one step: hi = RNE_fp16(P) and, when RES, the
+    // residual res = RNE_fp16((P - hi) * 2^11), so that hi + res * 2^-11
+    // carries P to about 22 bits.
+    struct Probs {
+        f16x8 hi[RT];
+        f16x8 res[RT];
+    };
+    auto softmax = [&](int32_t t_step, const Scores& sc, bool edge, Probs& pr) __attribute__((always_inline)) {
         float xs[RT][8];
         float smax[RT];
         bool need = false;
@@ -549,16 +571,23 @@ pfs_split_kernel(const SplitArgs a) {
         // finite: it only changes together with a finite m_ref)
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            f16x2 pp[4];
+            f16x2 pp[4], pr_res[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float c = edge ? 1.0f : cscale;
                 const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e], c, nb[nt]));
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e + 1], c, nb[nt]));
-                pp[e >> 1] = f16x2{(_Float16)p0, (_Float16)p1};
+                const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+                pp[e >> 1] = f16x2{h0, h1};
+                if constexpr (RES)  // p - hi is exact in FP32, and so is the scaling by 2^11
+                    pr_res[e >> 1] = f16x2{(_Float16)((p0 - (float)h0) * 2048.0f),
+                                           (_Float16)((p1 - (float)h1) * 2048.0f)};
             }
-            pop[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
-                                             bit_cast_<uint32_t>(pp[2]), bit_cast_<uint32_t>(pp[3])});
+            pr.hi[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
+                                               bit_cast_<uint32_t>(pp[2]), bit_cast_<uint32_t>(pp[3])});
+            if constexpr (RES)
+                pr.res[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pr_res[0]), bit_cast_<uint32_t>(pr_res[1]),
+                                                    bit_cast_<uint32_t>(pr_res[2]), bit_cast_<uint32_t>(pr_res[3])});
         }
     };
     // O^T += V^T * P^T for head_dim tiles [md0, md0 + 4), V^T read transposed from LDS
@@ -574,23 +603,34 @@ pfs_split_kernel(const SplitArgs a) {
         }
         return vc;
     };
-    auto pv_fold = [&](const VChunk& vc, int md0, const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
+    // (with RES, also O^T += (V^T * 2^-11) * RES^T into the same accumulators)
+    auto pv_fold = [&](const VChunk& vc, int md0, const Probs& pr) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f16x8 vop = fp8x8_to_f16x8<FMT>((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
-                acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], acc[md0 + u][nt], 0, 0, 0);
+                acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pr.hi[nt], acc[md0 + u][nt], 0, 0, 0);
+            if constexpr (RES) {
+                const f16x8 vres = e4m3x8_to_f16x8_res((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
+#pragma unroll
+                for (int nt = 0; nt < RT; ++nt)
+                    acc[md0 + u][nt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vres, pr.res[nt], acc[md0 + u][nt], 0, 0, 0);
+            }
         }
     };
-    auto pv_chunk = [&](const uint8_t* sbase, int md0, const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
-        pv_fold(v_read(sbase, md0), md0, pop);
+    auto pv_chunk = [&](const uint8_t* sbase, int md0, const Probs& pr) __attribute__((always_inline)) {
+        pv_fold(v_read(sbase, md0), md0, pr);
     };
-    // l += 1 * P^T (row sums from the same FP16 P)
-    auto row_sums = [&](const f16x8 (&pop)[RT]) __attribute__((always_inline)) {
+    // l += 1 * P^T (row sums from the same FP16 P; with RES, + 2^-11 * RES^T)
+    auto row_sums = [&](const Probs& pr) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nt = 0; nt < RT; ++nt)
-            lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
+        for (int nt = 0; nt < RT; ++nt) {
+            lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.hi[nt], lacc[nt], 0, 0, 0);
+            if constexpr (RES)
+                lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_res, pr.res[nt], lacc[nt], 0, 0, 0);
+        }
     };
 
     __syncthreads();  // tile table ready
@@ -601,7 +641,7 @@ pfs_split_kernel(const SplitArgs a) {
     if constexpr (PIPE) {
         // ---- NS - 2 stages in flight ahead of the one whose QK is folded ----
         Scores sc_cur;
-        f16x8 pop[RT];
+        Probs pop;
         wait_vm_and_barrier<(NS - 2) * NW>();  // stage 0 ready
         qk_zero(sc_cur);
 #pragma unroll
@@ -667,7 +707,7 @@ pfs_split_kernel(const SplitArgs a) {
                     const int32_t t_step = tok0 + st * kStep;
                     const uint8_t* sb = stage(kc);
                     Scores sc;
-                    f16x8 pop[RT];
+                    Probs pop;
                     qk_zero(sc);
 #pragma unroll
                     for (int j = 0; j < KLOADS; ++j) {
@@ -882,50 +922,50 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const Comb
 }
 
 
-template <int D, int RT, int RG, int FMT>
+template <int D, int RT, int RG, int FMT, bool RES>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
     constexpr int W = pfs::split_waves(D, RG);
     constexpr int TP = W / RG;
     constexpr int NS = pfs::split_stages(D, TP, W);
     const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
     const int64_t wgs = ((units + 7) / 8) * 8 * a.row_blocks;
-    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS, FMT>), dim3((unsigned)wgs), dim3(64 * W), 0, stream,
-                       a);
+    hipLaunchKernelGGL((pfs_split_kernel<D, RT, RG, TP, NS, FMT, RES>), dim3((unsigned)wgs), dim3(64 * W), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
 // Row groups above one occur only with the most row tiles a wave can hold.
-template <int D, int RT, int FMT>
+template <int D, int RT, int FMT, bool RES>
 hipError_t launch_split_rt(const SplitArgs& a, int32_t row_groups, hipStream_t stream) {
     if constexpr (RT > pfs::max_row_tiles(D)) {
         return hipErrorInvalidValue;
     } else {
-        if (row_groups == 1) return launch_split<D, RT, 1, FMT>(a, stream);
+        if (row_groups == 1) return launch_split<D, RT, 1, FMT, RES>(a, stream);
         if constexpr (RT == pfs::max_row_tiles(D)) {
-            if (row_groups == 2) return launch_split<D, RT, 2, FMT>(a, stream);
-            if (row_groups == 4) return launch_split<D, RT, 4, FMT>(a, stream);
+            if (row_groups == 2) return launch_split<D, RT, 2, FMT, RES>(a, stream);
+            if (row_groups == 4) return launch_split<D, RT, 4, FMT, RES>(a, stream);
         }
         return hipErrorInvalidValue;
     }
 }
 
-template <int D, int FMT>
+template <int D, int FMT, bool RES>
 hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t row_groups, hipStream_t stream) {
     switch (row_tiles) {
-        case 1: return launch_split_rt<D, 1, FMT>(a, row_groups, stream);
-        case 2: return launch_split_rt<D, 2, FMT>(a, row_groups, stream);
-        case 4: return launch_split_rt<D, 4, FMT>(a, row_groups, stream);
+        case 1: return launch_split_rt<D, 1, FMT, RES>(a, row_groups, stream);
+        case 2: return launch_split_rt<D, 2, FMT, RES>(a, row_groups, stream);
+        case 4: return launch_split_rt<D, 4, FMT, RES>(a, row_groups, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int FMT>
+template <int FMT, bool RES>
 hipError_t launch_split_fmt(const SplitArgs& a, int32_t head_dim, int32_t row_tiles, int32_t row_groups,
                             hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_split_d<64, FMT>(a, row_tiles, row_groups, stream);
-        case 128: return launch_split_d<128, FMT>(a, row_tiles, row_groups, stream);
-        case 256: return launch_split_d<256, FMT>(a, row_tiles, row_groups, stream);
+        case 64: return launch_split_d<64, FMT, RES>(a, row_tiles, row_groups, stream);
+        case 128: return launch_split_d<128, FMT, RES>(a, row_tiles, row_groups, stream);
+        case 256: return launch_split_d<256, FMT, RES>(a, row_tiles, row_groups, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -967,11 +1007,15 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256) return PFS_ERR_UNSUPPORTED;
     hipError_t e;
-    switch (p.kv_format) {
-        case PFS_KV_E4M3: e = launch_split_fmt<PFS_KV_E4M3>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s); break;
-        case PFS_KV_E5M2: e = launch_split_fmt<PFS_KV_E5M2>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s); break;
-        default: return PFS_ERR_UNSUPPORTED;
-    }
+    // the residual probabilities exist for E4M3 only (the plan rejects E5M2 with them)
+    if (p.kv_format == PFS_KV_E4M3 && p.pv_residual)
+        e = launch_split_fmt<PFS_KV_E4M3, true>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+    else if (p.kv_format == PFS_KV_E4M3)
+        e = launch_split_fmt<PFS_KV_E4M3, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+    else if (p.kv_format == PFS_KV_E5M2 && !p.pv_residual)
+        e = launch_split_fmt<PFS_KV_E5M2, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+    else
+        return PFS_ERR_UNSUPPORTED;
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
 

@@ -50,7 +50,7 @@ const char* pfs_status_string(int32_t status) {
         case PFS_OK: return "ok";
         case PFS_ERR_NULL: return "a required pointer is NULL";
         case PFS_ERR_SHAPE: return "inconsistent or out-of-range size or stride";
-        case PFS_ERR_UNSUPPORTED: return "unsupported head_dim, q, page size, partition size or KV format";
+        case PFS_ERR_UNSUPPORTED: return "unsupported head_dim, q, page size, partition size, KV format or probability mode";
         case PFS_ERR_ALIGNMENT: return "a KV stride or a base pointer is not 16-byte aligned";
         case PFS_ERR_HEAD_MAP: return "head map entry out of range or KV-head groups not uniform";
         case PFS_ERR_WORKSPACE: return "workspace NULL, misaligned (256 B) or too small";
@@ -82,6 +82,8 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
     if (p.page_size % 16 != 0) return PFS_ERR_UNSUPPORTED;
     if (p.partition_tokens != pfs::kPartitionTokens) return PFS_ERR_UNSUPPORTED;
     if (p.kv_format != PFS_KV_E4M3 && p.kv_format != PFS_KV_E5M2) return PFS_ERR_UNSUPPORTED;
+    if (p.pv_residual != 0 && p.pv_residual != 1) return PFS_ERR_UNSUPPORTED;
+    if (p.pv_residual && p.kv_format != PFS_KV_E4M3) return PFS_ERR_UNSUPPORTED;
     if (p.tokens_per_split < 0 || !is_multiple(p.tokens_per_split, p.partition_tokens))
         return PFS_ERR_SHAPE;
 

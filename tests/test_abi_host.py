@@ -86,6 +86,8 @@ def test_valid_problem_plans():
     (dict(partition_tokens=32), "PFS_ERR_UNSUPPORTED"),
     (dict(kv_format=2), "PFS_ERR_UNSUPPORTED"),
     (dict(kv_format=-1), "PFS_ERR_UNSUPPORTED"),
+    (dict(pv_residual=2), "PFS_ERR_UNSUPPORTED"),
+    (dict(pv_residual=1, kv_format=1), "PFS_ERR_UNSUPPORTED"),  # residual P needs E4M3-derived V
     (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
     (dict(num_q_heads=15, head_map=[0] * 15), "PFS_ERR_SHAPE"),
     (dict(batch=-1), "PFS_ERR_SHAPE"),
@@ -110,6 +112,13 @@ def test_both_kv_formats_plan_identically():
     assert (a.num_splits, a.tokens_per_split, a.workspace_bytes) == (b.num_splits, b.tokens_per_split,
                                                                       b.workspace_bytes)
     assert (a.kv_format, b.kv_format) == (0, 1)
+
+
+def test_residual_probabilities_plan_like_the_default():
+    a, b = _lib.Plan(**BASE), _lib.Plan(**dict(BASE, pv_residual=1))
+    assert (a.num_splits, a.tokens_per_split, a.workspace_bytes) == (b.num_splits, b.tokens_per_split,
+                                                                      b.workspace_bytes)
+    assert (a.pv_residual, b.pv_residual) == (0, 1)
 
 
 def test_head_major_pool_layout_is_accepted():
@@ -196,5 +205,5 @@ def test_plan_create_null_arguments():
     lib = _lib.load()
     h = ctypes.c_void_p()
     assert lib.pfs_plan_create(None, ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
-    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 64 * 512, 512, 256, 0.0625, None)
+    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 0, 64 * 512, 512, 256, 0.0625, None)
     assert lib.pfs_plan_create(ctypes.byref(prob), ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
