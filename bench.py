@@ -7,13 +7,18 @@ E4M3 K/V with per-head scales and 1% outlier tokens, page size 64 (the
 256K-context q8 case the metric is quoted on). Inputs are synthetic, seeded and
 resident in HBM before the timed region starts.
 
-Timing: W untimed warmup steps, then K timed steps. Before every timed step an
-untimed read of a clean 1 GiB buffer evicts the 256 MB Infinity Cache and the
-L2s, so the KV bytes come from HBM. The scrub only reads: a scrub that writes
-leaves dirty lines whose write-back then competes with the timed kernel's
-reads. Each step is bracketed by HIP events recorded on the stream the kernels
-run on (split: e0 -> e1, combine: e1 -> e2). The whole timed loop is also
-bracketed by a device synchronize.
+Timing: W untimed warmup steps, then K timed steps (split and combine
+launched back to back). Before every step an untimed read of a clean 1 GiB
+buffer evicts the 256 MB Infinity Cache and the L2s, so the KV bytes come from
+HBM. The scrub only reads: a scrub that writes leaves dirty lines whose
+write-back then competes with the timed kernel's reads. Each step is
+bracketed by HIP events recorded on the stream the kernels run on, and the
+whole timed loop by a device synchronize. A second pass puts an event between
+the kernels as well (e0 -> e1 -> e2) for the per-kernel figures: the split
+kernel's mean launch time is the roofline's denominator. That middle event
+delays the combine's start by a few microseconds, which is why the step is
+timed without it. A third pass replays the step captured as one HIP graph
+(reported beside the main figure).
 
 Prints one JSON line. `value` is the achieved KV read rate: live K+V bytes of
 the step divided by the mean step time.
@@ -142,9 +147,13 @@ def codec_timing(w, t, dev, evict, reps: int = 20) -> dict:
     }
 
 
-def time_steps(split, combine, evict, stream, steps: int, warmup: int):
+def time_steps(split, combine, evict, stream, steps: int, warmup: int, mid_event: bool):
     """Warm up, then time `steps` scrubbed split + combine steps with HIP
-    events on `stream`. Returns (split_ms, combine_ms, step_ms, wall_s)."""
+    events on `stream`. With `mid_event` an event between the two kernels
+    also splits each step into its kernels (that event delays the combine's
+    start by a few microseconds, so the step itself is timed without it).
+    Returns (split_ms, combine_ms, step_ms, wall_s); the first two are None
+    without `mid_event`."""
     import numpy as np
     import torch
 
@@ -161,15 +170,42 @@ def time_steps(split, combine, evict, stream, steps: int, warmup: int):
         evict()
         evs[k][0].record(stream)
         split()
-        evs[k][1].record(stream)
+        if mid_event:
+            evs[k][1].record(stream)
         combine()
         evs[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    if not mid_event:
+        return None, None, step_ms, wall
     split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     return split_ms, comb_ms, step_ms, wall
+
+
+def time_graph(graph, evict, stream, steps: int, warmup: int):
+    """Warm up, then time `steps` replays of `graph`, each after an untimed
+    scrub, with HIP events around each replay on `stream`. Returns
+    (step_ms, wall_s)."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        evict()
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for k in range(steps):
+        evict()
+        evs[k][0].record(stream)
+        graph.replay()
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    return np.array([e[0].elapsed_time(e[1]) for e in evs]), wall
 
 
 def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3", pv_residual: bool = False,
@@ -196,7 +232,8 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
     split = lambda: _lib.verify_split(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["block_table"],
                                       t["live_len"], ws, stream)
     combine = lambda: _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
-    split_ms, comb_ms, step_ms, _ = time_steps(split, combine, evict, stream, steps, warmup)
+    _, _, step_ms, _ = time_steps(split, combine, evict, stream, steps, warmup, mid_event=False)
+    split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, steps, 0, mid_event=True)
     sb = split_algorithmic_bytes(w, plan)
     ach = sb / (float(split_ms.mean()) * 1e-3) / 1e9
     res = {
@@ -306,17 +343,25 @@ def main() -> int:
         _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
 
     note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B")
-    split_ms, comb_ms, step_ms, wall = time_steps(split, combine, evict, stream, args.steps, args.warmup)
+    # the timed steps: split and combine launched back to back, HIP events
+    # around each step on the kernels' stream
+    _, _, step_ms, wall = time_steps(split, combine, evict, stream, args.steps, args.warmup, mid_event=False)
     y = out.cpu().numpy()
     out_sha = hashlib.sha256(y.tobytes()).hexdigest()
+    # per-kernel figures: a second pass with an event between the kernels (the
+    # split kernel's launch time is the roofline's denominator)
+    split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, args.steps, 0, mid_event=True)
 
-    # the same step as one HIP graph, replayed back to back (cache-warm: context only)
+    # the same step captured as one HIP graph, each replay after the scrub
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         _lib.verify(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
                     t["live_len"], out, ws)
-    g.replay()
     torch.cuda.synchronize()
+    graph_step_ms, _ = time_graph(g, evict, stream, args.steps, 3)
+    same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
+
+    # the same graph replayed back to back without scrubs (cache-warm: context only)
     ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 50
     ga.record()
@@ -325,7 +370,6 @@ def main() -> int:
     gb.record()
     torch.cuda.synchronize()
     graph_warm_ms = ga.elapsed_time(gb) / reps
-    same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
 
     kv = w.kv_bytes()
     mean_ms = float(step_ms.mean())
@@ -378,6 +422,7 @@ def main() -> int:
             "mean_launch_us": round(split_mean_ms * 1e3, 2),
         },
         "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
+        "us_per_step_graph": round(float(graph_step_ms.mean()) * 1e3, 2),
         "graph_replay_cache_warm_us": round(graph_warm_ms * 1e3, 2),
         "graph_output_matches_eager": bool(same),
         "timed_loop_wall_s": round(wall, 4),

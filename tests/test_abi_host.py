@@ -89,6 +89,7 @@ def test_valid_problem_plans():
     (dict(pv_residual=2), "PFS_ERR_UNSUPPORTED"),
     (dict(pv_residual=1, kv_format=1), "PFS_ERR_UNSUPPORTED"),  # residual P needs E4M3-derived V
     (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
+    (dict(tokens_per_split=16384 + 64), "PFS_ERR_UNSUPPORTED"),  # beyond the split's 1024-tile table
     (dict(num_q_heads=15, head_map=[0] * 15), "PFS_ERR_SHAPE"),
     (dict(batch=-1), "PFS_ERR_SHAPE"),
     (dict(batch=65536), "PFS_ERR_SHAPE"),
@@ -104,6 +105,11 @@ def test_valid_problem_plans():
 ])
 def test_invalid_problems_are_rejected(over, status):
     assert plan_status(**over) == _lib.STATUS_CODE[status]
+
+
+def test_largest_split_is_accepted():
+    p = _lib.Plan(**dict(BASE, tokens_per_split=16384))
+    assert p.tokens_per_split == 16384 and p.num_splits == 4096 * 64 // 16384
 
 
 def test_both_kv_formats_plan_identically():

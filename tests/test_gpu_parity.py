@@ -206,3 +206,43 @@ def test_two_streams_two_workspaces():
         o2 = run(w, tensors=t, stream=s2)[0]
     torch.cuda.synchronize()
     assert np.array_equal(to_np(o1).view(np.uint16), to_np(o2).view(np.uint16))
+
+
+def _golden_page_sizes():
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_sizes.json")
+    with open(path) as f:
+        return json.load(f)["page_sizes"]
+
+
+@pytest.mark.parametrize("page", _golden_page_sizes())
+def test_page_sizes_of_the_pages(page):
+    """The page sizes the pages run (none a power of two): GQA6 at head_dim
+    256, q5, contexts that span several pages and end inside one."""
+    w = W.build(seed=page, batch=2, q=5, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=page,
+                lengths=[3 * page + 37, page - 3])
+    log(f"[page] {page} lengths={w.live_len.tolist()}")
+    for tps in (0, 640):
+        judge(to_np(run(w, tokens_per_split=tps)[0]), oracle_ref(w), f"page {page} tps={tps}")
+
+
+def test_largest_split_uses_the_whole_tile_table():
+    """tokens_per_split = 16384, the most a split addresses (1024 tiles of 16
+    tokens): two full splits and a ragged third."""
+    w = W.build(seed=71, batch=1, q=8, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=64,
+                lengths=[2 * 16384 + 1000])
+    log("[tps] 16384")
+    judge(to_np(run(w, tokens_per_split=16384)[0]), oracle_ref(w), "tps 16384")
+
+
+def test_most_rows_per_kv_head():
+    """q = 16 draft rows x 16 query heads per KV head = 256 rows: four row
+    blocks of 64 at head_dim 256, and the most query heads (256) at head_dim 64."""
+    w = W.build(seed=72, batch=1, q=16, num_q_heads=16, num_kv_heads=1, head_dim=256, page_size=64,
+                lengths=[1500])
+    judge(to_np(run(w)[0]), oracle_ref(w), "256 rows d256")
+    w2 = W.build(seed=73, batch=1, q=2, num_q_heads=256, num_kv_heads=2, head_dim=64, page_size=16,
+                 lengths=[700])
+    judge(to_np(run(w2)[0]), oracle_ref(w2), "256 query heads d64")
