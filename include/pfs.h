@@ -138,8 +138,9 @@ const char* pfs_status_string(int32_t status);
  * head_dim / q / page size / partition support, 16-byte stride alignment
  * (the pages' counterexample, token stride 264 with a 16-byte paired loader,
  * is rejected here with PFS_ERR_ALIGNMENT), non-overlapping nesting of the
- * strides, and a uniform head map (every KV head serves exactly
- * num_q_heads / num_kv_heads query heads).
+ * strides, a uniform head map (every KV head serves exactly
+ * num_q_heads / num_kv_heads query heads), and a split grid below 2^31
+ * work-items (PFS_ERR_SHAPE otherwise).
  * The plan is immutable and may be shared by host threads.
  */
 int32_t pfs_plan_create(const pfs_problem* problem, pfs_plan** out);
@@ -209,7 +210,9 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
  * E4M3 and E5M2 value is an FP16 number). NaN codes give NaN, E5M2
  * infinities give infinities. Same alignment and precondition rules as
  * pfs_verify; no workspace. Only the plan's batch, num_kv_heads, head_dim,
- * page size, max_pages_per_row, strides and KV format are used.
+ * page size, max_pages_per_row, strides and KV format are used;
+ * capacity * num_kv_heads * head_dim / 16 must stay below 2^31
+ * (PFS_ERR_SHAPE otherwise).
  */
 int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float* scale,
                           const int32_t* block_table, const int32_t* live_len, void* out_fp16,

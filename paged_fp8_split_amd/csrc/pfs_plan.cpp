@@ -157,6 +157,14 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
     if (tps > round_up(capacity, pfs::kPartitionTokens)) tps = round_up(capacity, pfs::kPartitionTokens);
     plan->tokens_per_split = (int32_t)tps;
     plan->num_splits = (int32_t)((capacity + tps - 1) / tps);
+    // the split grid (work-items in one dimension, 32-bit index math on the
+    // device) must stay below 2^31
+    const int64_t units = (int64_t)plan->num_splits * p.num_kv_heads * (p.batch > 0 ? p.batch : 1);
+    const int64_t split_items = ((units + 7) / 8) * 8 * plan->row_blocks * 64 * plan->waves;
+    if (split_items > (int64_t)INT32_MAX) {
+        delete plan;
+        return PFS_ERR_SHAPE;
+    }
 
     const int64_t slots = (int64_t)plan->num_splits * (p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->rows;
     plan->ws_ml_offset = 0;
@@ -246,6 +254,9 @@ int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float
     if (!pool || !block_table || !live_len || !out_fp16) return PFS_ERR_NULL;
     if (((uintptr_t)pool | (uintptr_t)out_fp16) & 15u) return PFS_ERR_ALIGNMENT;
     if (((uintptr_t)block_table | (uintptr_t)live_len | (uintptr_t)scale) & 3u) return PFS_ERR_ALIGNMENT;
+    // one work-item per 16 bytes of a request's rows: the grid's x extent
+    if ((int64_t)plan->capacity * plan->p.num_kv_heads * (plan->p.head_dim / 16) > (int64_t)INT32_MAX)
+        return PFS_ERR_SHAPE;
     return pfs_launch_bridge(plan, pool, scale, block_table, live_len, out_fp16, stream);
 }
 

@@ -90,6 +90,8 @@ def test_valid_problem_plans():
     (dict(pv_residual=1, kv_format=1), "PFS_ERR_UNSUPPORTED"),  # residual P needs E4M3-derived V
     (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
     (dict(tokens_per_split=16384 + 64), "PFS_ERR_UNSUPPORTED"),  # beyond the split's 1024-tile table
+    # 65535 requests x 2 KV heads x 1024 splits of 64 tokens: a split grid beyond 2^31 work-items
+    (dict(batch=65535, max_pages_per_row=1024, tokens_per_split=64), "PFS_ERR_SHAPE"),
     (dict(num_q_heads=15, head_map=[0] * 15), "PFS_ERR_SHAPE"),
     (dict(batch=-1), "PFS_ERR_SHAPE"),
     (dict(batch=65536), "PFS_ERR_SHAPE"),
@@ -213,3 +215,25 @@ def test_plan_create_null_arguments():
     assert lib.pfs_plan_create(None, ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
     prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 0, 64 * 512, 512, 256, 0.0625, None)
     assert lib.pfs_plan_create(ctypes.byref(prob), ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+
+
+def test_codec_host_checks_need_no_device():
+    lib = _lib.load()
+    ok = 1 << 20
+    p = _lib.Plan(**BASE)
+    # bridge: NULL, misaligned pool or output, misaligned scale
+    assert lib.pfs_dequant_paged(p.handle, None, None, ok, ok, ok, None) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    assert lib.pfs_dequant_paged(p.handle, ok + 8, None, ok, ok, ok, None) == _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    assert lib.pfs_dequant_paged(p.handle, ok, ok + 2, ok, ok, ok, None) == _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    # bridge grid: capacity x KV heads x head_dim / 16 work-items must stay below 2^31
+    big = _lib.Plan(**dict(BASE, max_pages_per_row=1 << 20, num_pool_pages=1 << 20))
+    assert lib.pfs_dequant_paged(big.handle, ok, None, ok, ok, ok, None) == _lib.STATUS_CODE["PFS_ERR_SHAPE"]
+    # append: NULL and misaligned arguments
+    assert lib.pfs_kv_append(p.handle, None, *([ok] * 7), None) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    assert lib.pfs_kv_append(p.handle, ok + 8, *([ok] * 7), None) == _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    assert lib.pfs_kv_append(p.handle, *([ok] * 2), ok + 2, *([ok] * 5), None) == \
+        _lib.STATUS_CODE["PFS_ERR_ALIGNMENT"]
+    # an empty batch touches nothing
+    e = _lib.Plan(**dict(BASE, batch=0))
+    assert lib.pfs_dequant_paged(e.handle, None, None, None, None, None, None) == 0
+    assert lib.pfs_kv_append(e.handle, *([None] * 8), None) == 0
