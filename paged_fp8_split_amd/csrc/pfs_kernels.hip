@@ -824,29 +824,33 @@ struct CombineArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// One workgroup of 256 threads per (request, KV head, row, 64-column slice),
-// so that even one request's few rows spread over every CU. Thread t owns the
-// 4 columns 4 (t % 16) .. of the slice and the visible splits s with
-// s % 16 == t / 16 (its split lane), folded in ascending order CH at a time
-// (their loads are issued together) against a running maximum; the 16 split
-// lanes of each column group are then merged in lane order against the
-// global maximum.
+// One workgroup of 256 threads per (request, KV head, row, column slice), so
+// that even one request's few rows spread over every CU. With SL split lanes
+// (16, or 8 / 4 when the plan has that few splits) a workgroup covers
+// 1024 / SL columns: thread t owns the 4 columns 4 (t % (256 / SL)) .. of the
+// slice and the visible splits s with s % SL == t / (256 / SL) (its split
+// lane), folded in ascending order CH at a time (their loads are issued
+// together) against a running maximum; the SL split lanes of each column
+// group are then merged in lane order against the global maximum. Fewer lanes
+// for few splits keep the workgroup count (and the idle lanes) down.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineSplitLanes = 16;
 constexpr int kCombineChunk = 8;
 
-template <int D>
+template <int D, int SL>
 __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const CombineArgs a) {
-    constexpr int SL = kCombineSplitLanes, CH = kCombineChunk, SLICES = D / 64;
-    __shared__ float part_m[SL][16];
-    __shared__ float part_l[SL][16];
-    __shared__ f32x4 part_acc[SL][16];
+    constexpr int CH = kCombineChunk;
+    constexpr int CG = kCombineThreads / SL;  // 4-column groups per workgroup
+    constexpr int SLICES = D / (4 * CG);
+    static_assert(SLICES >= 1 && D % (4 * CG) == 0, "combine slice");
+    __shared__ float part_m[SL][CG];
+    __shared__ float part_l[SL][CG];
+    __shared__ f32x4 part_acc[SL][CG];
 
     const int t = threadIdx.x;
-    const int cg = t % 16;  // column group of the slice
-    const int sl = t / 16;  // split lane
+    const int cg = t % CG;  // column group of the slice
+    const int sl = t / CG;  // split lane
     const int r = blockIdx.x / SLICES;
-    const int col0 = (blockIdx.x % SLICES) * 64 + 4 * cg;
+    const int col0 = (blockIdx.x % SLICES) * (4 * CG) + 4 * cg;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
     const int i = r / a.group;
@@ -1038,11 +1042,20 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.tokens_per_split = plan->tokens_per_split;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid(plan->rows * (p.head_dim / 64), p.num_kv_heads, p.batch);
-    switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, dim3(kCombineThreads), 0, s, ca); break;
-        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, dim3(kCombineThreads), 0, s, ca); break;
-        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, dim3(kCombineThreads), 0, s, ca); break;
+    // split lanes: as few as the plan's splits need (wider column slices, fewer
+    // workgroups), at most 16, and a slice no wider than head_dim
+    int sl = 16;
+    if (plan->num_splits <= 4 && p.head_dim >= 256) sl = 4;
+    else if (plan->num_splits <= 8 && p.head_dim >= 128) sl = 8;
+    const dim3 grid(plan->rows * (p.head_dim * sl / 1024), p.num_kv_heads, p.batch);
+    const dim3 block(kCombineThreads);
+    switch (p.head_dim * 100 + sl) {
+        case 6416: hipLaunchKernelGGL((pfs_combine_kernel<64, 16>), grid, block, 0, s, ca); break;
+        case 12816: hipLaunchKernelGGL((pfs_combine_kernel<128, 16>), grid, block, 0, s, ca); break;
+        case 12808: hipLaunchKernelGGL((pfs_combine_kernel<128, 8>), grid, block, 0, s, ca); break;
+        case 25616: hipLaunchKernelGGL((pfs_combine_kernel<256, 16>), grid, block, 0, s, ca); break;
+        case 25608: hipLaunchKernelGGL((pfs_combine_kernel<256, 8>), grid, block, 0, s, ca); break;
+        case 25604: hipLaunchKernelGGL((pfs_combine_kernel<256, 4>), grid, block, 0, s, ca); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
