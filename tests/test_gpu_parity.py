@@ -246,3 +246,69 @@ def test_most_rows_per_kv_head():
     w2 = W.build(seed=73, batch=1, q=2, num_q_heads=256, num_kv_heads=2, head_dim=64, page_size=16,
                  lengths=[700])
     judge(to_np(run(w2)[0]), oracle_ref(w2), "256 query heads d64")
+
+
+def test_lengths_at_split_partition_and_tile_edges():
+    """One batch whose live lengths sit on and beside every boundary the kernel
+    has: 16-token tiles, 32-token steps, 64-token partitions, 256-token splits."""
+    lengths = [1, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513]
+    w = W.build(seed=74, batch=len(lengths), q=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                lengths=lengths)
+    r = oracle_ref(w)
+    for tps in (0, 256, 64):
+        judge(to_np(run(w, tokens_per_split=tps)[0]), r, f"edge lengths tps={tps}")
+
+
+def test_speculative_steps_in_one_graph():
+    """append (quantize-on-write of the draft tokens) + verify captured as one
+    HIP graph and replayed for successive steps: the live length grows by q
+    and new draft K/V arrive each step; every replay equals the eager calls
+    and the oracle on the host-updated pools."""
+    import torch
+
+    q = 8
+    w = W.build(seed=75, batch=2, q=q, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                lengths=[4096, 4096], capacity=4096)
+    w.live_len = np.array([1000, 2900], np.int32)
+    dev = device()
+    t = W.device_tensors(w, dev)
+    rng = np.random.default_rng(76)
+    kn = torch.zeros((2, q, 2, 256), dtype=torch.float16, device=dev)
+    vn = torch.zeros_like(kn)
+    out = torch.empty_like(t["q"])
+    plan = pfs.make_plan(batch=w.batch, q=q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
+                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"])
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        pfs.kv_append(kn, vn, t["k_scale"], t["v_scale"], t["block_table"], t["live_len"], t["k_pool"], t["v_pool"])
+        run(w, tensors=t, out=out, workspace=ws)
+
+    step()  # warm up the plan cache before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    host = w.copy()
+    k_dev0, v_dev0 = t["k_pool"].clone(), t["v_pool"].clone()
+    for s in range(4):
+        knp = rng.normal(0, 1, (2, q, 2, 256)).astype(np.float16)
+        vnp = rng.normal(0, 1, (2, q, 2, 256)).astype(np.float16)
+        host.live_len = (w.live_len + q * s).astype(np.int32)
+        kn.copy_(torch.from_numpy(knp))
+        vn.copy_(torch.from_numpy(vnp))
+        t["live_len"].copy_(torch.from_numpy(host.live_len))
+        k_before, v_before = t["k_pool"].clone(), t["v_pool"].clone()
+        out.fill_(1)
+        g.replay()
+        yg = to_np(out).copy()
+        kg, vg = t["k_pool"].clone(), t["v_pool"].clone()
+        # the same step eagerly from the same pools
+        t["k_pool"].copy_(k_before)
+        t["v_pool"].copy_(v_before)
+        step()
+        assert np.array_equal(to_np(out).view(np.uint16), yg.view(np.uint16)), f"step {s}"
+        assert torch.equal(kg, t["k_pool"]) and torch.equal(vg, t["v_pool"]), f"step {s} pools"
+        host.k_pool, host.v_pool = oracle.kv_append(host, knp, vnp)
+        judge(yg, oracle_ref(host), f"graph step {s} lengths {host.live_len.tolist()}")
+    del k_dev0, v_dev0
