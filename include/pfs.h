@@ -168,8 +168,10 @@ int32_t pfs_plan_tokens_per_split(const pfs_plan* plan);
  *                at a time (stream order).
  * Device-side preconditions (not checked on the host, which must not
  * synchronize): live_len values are clamped into [0, capacity]; block-table
- * entries are read only for logical pages below ceil(L_b / page_size) and
- * must lie in [0, num_pool_pages); live K/V bytes are finite codes of the
+ * entries of logical pages below ceil(L_b / page_size) must lie in
+ * [0, num_pool_pages) (only those are used to address the pools; the split
+ * kernel may read other entries of the row before the live length is known,
+ * and ignores them); live K/V bytes are finite codes of the
  * plan's KV format (bytes no live token owns may hold anything, NaN and
  * infinity codes included).
  * All buffers are caller-owned. Returns PFS_OK or an error status; a launch

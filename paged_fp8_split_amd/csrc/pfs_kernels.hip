@@ -294,8 +294,15 @@ pfs_split_kernel(const SplitArgs a) {
     const int g = (unit / a.num_splits) % a.num_kv_heads;
     const int b = unit / (a.num_splits * a.num_kv_heads);
 
-    const int32_t L = __builtin_amdgcn_readfirstlane(clamp_i(a.live_len[b], 0, a.capacity));
     const int32_t tok0 = split * a.tokens_per_split;
+    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+    // the first block-table entry this thread resolves, read before the live
+    // length is known (any token below the capacity has an entry) so that the
+    // two reads overlap
+    const int32_t t_first = tok0 + 16 * (int)threadIdx.x;
+    const int32_t pg_first = t_first / a.page_size;
+    const int32_t page_first = (t_first < a.capacity && 16 * (int)threadIdx.x < a.tokens_per_split) ? bt_row[pg_first] : 0;
+    const int32_t L = __builtin_amdgcn_readfirstlane(clamp_i(a.live_len[b], 0, a.capacity));
     if (tok0 >= L) return;  // nothing live in this split: the combine never reads it
     const int32_t tok_end = min(tok0 + a.tokens_per_split, L);
     const int32_t nsteps = (tok_end - tok0 + kStep - 1) / kStep;
@@ -305,13 +312,13 @@ pfs_split_kernel(const SplitArgs a) {
     // ---- tile table: pool byte offset of every 16-token tile of the split ----
     {
         const int64_t head_off = (int64_t)g * a.head_stride;
-        const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
         const int32_t ntiles = min((tok_end - tok0 + 15) / 16, pfs::kTileTableEntries);
         for (int e = threadIdx.x; e < ntiles; e += 64 * W) {
             const int32_t t0 = tok0 + 16 * e;
             const int32_t pg = t0 / a.page_size;
             const int32_t slot = t0 - pg * a.page_size;
-            tile_off[e] = (int64_t)bt_row[pg] * a.page_stride + (int64_t)slot * a.token_stride + head_off;
+            const int32_t page = e == (int)threadIdx.x ? page_first : bt_row[pg];
+            tile_off[e] = (int64_t)page * a.page_stride + (int64_t)slot * a.token_stride + head_off;
         }
     }
 
