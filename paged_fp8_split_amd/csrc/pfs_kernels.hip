@@ -365,12 +365,21 @@ pfs_split_kernel(const SplitArgs a) {
 
     f32x4 acc[MD][RT];
     f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
+    // with RES at head_dim 256: the residual products go to accumulators of
+    // their own (against the unscaled V operand) and are folded in times
+    // 2^-11 after the last step
+    constexpr bool RES_ACC = RES && D == 256;
+    f32x4 acc_res[RES_ACC ? MD : 1][RT];
+    f32x4 lacc_res[RT];
     float mref[RT], nb[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
         mref[nt] = -INFINITY;
         nb[nt] = 0.0f;
         lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lacc_res[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int md = 0; md < (RES_ACC ? MD : 1); ++md) acc_res[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int md = 0; md < MD; ++md) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -569,6 +578,11 @@ pfs_split_kernel(const SplitArgs a) {
                     lacc[nt] *= al;
 #pragma unroll
                     for (int md = 0; md < MD; ++md) acc[md][nt] *= al;
+                    if constexpr (RES_ACC) {
+                        lacc_res[nt] *= al;
+#pragma unroll
+                        for (int md = 0; md < MD; ++md) acc_res[md][nt] *= al;
+                    }
                     mref[nt] = m_new;
                     nb[nt] = kPBias - m_new;
                 }
@@ -618,7 +632,12 @@ pfs_split_kernel(const SplitArgs a) {
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
                 acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pr.hi[nt], acc[md0 + u][nt], 0, 0, 0);
-            if constexpr (RES) {
+            if constexpr (RES_ACC) {
+#pragma unroll
+                for (int nt = 0; nt < RT; ++nt)
+                    acc_res[md0 + u][nt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pr.res[nt], acc_res[md0 + u][nt], 0, 0, 0);
+            } else if constexpr (RES) {
                 const f16x8 vres = e4m3x8_to_f16x8_res((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
 #pragma unroll
                 for (int nt = 0; nt < RT; ++nt)
@@ -635,7 +654,9 @@ pfs_split_kernel(const SplitArgs a) {
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
             lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.hi[nt], lacc[nt], 0, 0, 0);
-            if constexpr (RES)
+            if constexpr (RES_ACC)
+                lacc_res[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.res[nt], lacc_res[nt], 0, 0, 0);
+            else if constexpr (RES)
                 lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_res, pr.res[nt], lacc[nt], 0, 0, 0);
         }
     };
@@ -733,6 +754,14 @@ pfs_split_kernel(const SplitArgs a) {
         }
     }
     wait_vm_and_barrier<0>();  // no load into LDS is still in flight
+    if constexpr (RES_ACC) {  // fold the residual products in (times 2^-11, exact in FP32)
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) {
+            lacc[nt] += lacc_res[nt] * (1.0f / 2048.0f);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) acc[md][nt] += acc_res[md][nt] * (1.0f / 2048.0f);
+        }
+    }
 
     // ---- merge the TP token lanes of each row group: ((tl0 + tl2) + (tl1 + tl3)) ... ----
     const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
