@@ -55,7 +55,10 @@
 // matrix core (a ones row times the same FP16 P the PV product uses); V's
 // scale is applied once in the combine. Masked scores are selected to -inf and
 // K/V bytes beyond the live length are never loaded (zero), so NaN (or E5M2
-// infinity) tail bytes cannot leak.
+// infinity) tail bytes cannot leak. With RES (high/residual probabilities,
+// "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+// historical scope) each P is also carried as an FP16 residual scaled by
+// 2^11, multiplied with V and folded in times 2^-11, so P reaches ~22 bits.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
