@@ -863,15 +863,14 @@ struct CombineArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// One workgroup of 256 threads per (request, KV head, row, column slice), so
-// that even one request's few rows spread over every CU. With SL split lanes
-// (16, or 8 / 4 when the plan has that few splits) a workgroup covers
-// 1024 / SL columns: thread t owns the 4 columns 4 (t % (256 / SL)) .. of the
-// slice and the visible splits s with s % SL == t / (256 / SL) (its split
-// lane), folded in ascending order CH at a time (their loads are issued
-// together) against a running maximum; the SL split lanes of each column
-// group are then merged in lane order against the global maximum. Fewer lanes
-// for few splits keep the workgroup count (and the idle lanes) down.
+// Many splits: one workgroup of 256 threads per (request, KV head, row,
+// column slice), so that even one request's few rows spread over every CU.
+// With SL split lanes a workgroup covers 1024 / SL columns: thread t owns the
+// 4 columns 4 (t % (256 / SL)) .. of the slice and the visible splits s with
+// s % SL == t / (256 / SL) (its split lane), folded in ascending order CH at a
+// time (their loads are issued together) against a running maximum; the SL
+// split lanes of each column group are then merged in lane order against the
+// global maximum. Plans with at most CH splits use pfs_combine_rows_kernel.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChunk = 8;
 
@@ -964,6 +963,72 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const Comb
     for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((num[c] * vs) / lt);
 }
 
+
+// Few splits: one thread per 4 columns of one row folds every visible split
+// of that row itself (in ascending order, CH loads issued together, running
+// maximum) with no cross-lane merge; a workgroup covers 1024 / D whole rows.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void pfs_combine_rows_kernel(const CombineArgs a) {
+    constexpr int CH = kCombineChunk;
+    constexpr int TPR = D / 4;                   // threads per row
+    constexpr int RPW = kCombineThreads / TPR;   // rows per workgroup
+    const int t = threadIdx.x;
+    const int r = blockIdx.x * RPW + t / TPR;
+    if (r >= a.rows) return;
+    const int col0 = 4 * (t % TPR);
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int i = r / a.group;
+    const int h = a.qhead[g * a.group + (r % a.group)];
+    _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + col0;
+    const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
+    const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
+    if (n == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = (_Float16)0.0f;
+        return;
+    }
+    const int ns = (n + a.tokens_per_split - 1) / a.tokens_per_split;
+    const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;
+    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+    float M = -INFINITY, lw = 0.0f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < ns; c0 += CH) {
+        float2 v[CH];
+        f32x4 x[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int sp = c0 + u;
+            if (sp < ns) {
+                const int64_t slot = slot0 + sp * stride;
+                v[u] = ml[slot];
+                x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + col0);
+            } else {
+                v[u] = make_float2(-INFINITY, 0.0f);
+                x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float cm = M;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) cm = fmaxf(cm, v[u].x);
+        if (cm != M) {
+            const float al = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
+            lw *= al;
+            acc *= al;
+            M = cm;
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const float f = (v[u].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[u].x - M);
+            lw += f * v[u].y;
+            acc += f * x[u];
+        }
+    }
+    const float vs = a.vscale[g];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((acc[c] * vs) / lw);
+}
 
 template <int D, int RT, int RG, int FMT, bool RES>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
@@ -1081,20 +1146,25 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.tokens_per_split = plan->tokens_per_split;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // split lanes: as few as the plan's splits need (wider column slices, fewer
-    // workgroups), at most 16, and a slice no wider than head_dim
-    int sl = 16;
-    if (plan->num_splits <= 4 && p.head_dim >= 256) sl = 4;
-    else if (plan->num_splits <= 8 && p.head_dim >= 128) sl = 8;
-    const dim3 grid(plan->rows * (p.head_dim * sl / 1024), p.num_kv_heads, p.batch);
+    if (plan->num_splits <= kCombineChunk) {  // every split of a row in one round of loads
+        const dim3 rgrid((plan->rows * p.head_dim / 4 + kCombineThreads - 1) / kCombineThreads, p.num_kv_heads,
+                         p.batch);
+        switch (p.head_dim) {
+            case 64: hipLaunchKernelGGL(pfs_combine_rows_kernel<64>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
+            case 128: hipLaunchKernelGGL(pfs_combine_rows_kernel<128>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
+            case 256: hipLaunchKernelGGL(pfs_combine_rows_kernel<256>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
+            default: return PFS_ERR_UNSUPPORTED;
+        }
+        return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
+    }
+    // more splits: 16 split lanes per column group, 64-column slices
+    constexpr int SL = 16;
+    const dim3 grid(plan->rows * (p.head_dim * SL / 1024), p.num_kv_heads, p.batch);
     const dim3 block(kCombineThreads);
-    switch (p.head_dim * 100 + sl) {
-        case 6416: hipLaunchKernelGGL((pfs_combine_kernel<64, 16>), grid, block, 0, s, ca); break;
-        case 12816: hipLaunchKernelGGL((pfs_combine_kernel<128, 16>), grid, block, 0, s, ca); break;
-        case 12808: hipLaunchKernelGGL((pfs_combine_kernel<128, 8>), grid, block, 0, s, ca); break;
-        case 25616: hipLaunchKernelGGL((pfs_combine_kernel<256, 16>), grid, block, 0, s, ca); break;
-        case 25608: hipLaunchKernelGGL((pfs_combine_kernel<256, 8>), grid, block, 0, s, ca); break;
-        case 25604: hipLaunchKernelGGL((pfs_combine_kernel<256, 4>), grid, block, 0, s, ca); break;
+    switch (p.head_dim) {
+        case 64: hipLaunchKernelGGL((pfs_combine_kernel<64, SL>), grid, block, 0, s, ca); break;
+        case 128: hipLaunchKernelGGL((pfs_combine_kernel<128, SL>), grid, block, 0, s, ca); break;
+        case 256: hipLaunchKernelGGL((pfs_combine_kernel<256, SL>), grid, block, 0, s, ca); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
