@@ -833,7 +833,8 @@ pfs_split_kernel(const SplitArgs a) {
         if (tl != 0) return;
     }
 
-    // ---- emit the split partial: (reference max, sum) and the unnormalized PV ----
+    // ---- emit the split partial: (reference max, sum) and the unnormalized PV
+    // (non-temporal stores: the combine reads them once, from beyond the L2) ----
     // accumulator element i of d tile md is column 16 md + 4 lg + i of row r
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
@@ -842,7 +843,7 @@ pfs_split_kernel(const SplitArgs a) {
         if (lg == 0) reinterpret_cast<float2*>(a.ws_ml)[slot_base + r] = make_float2(mref[nt], Ltot[nt]);
         float* dst = a.ws_acc + (slot_base + r) * D + 4 * lg;
 #pragma unroll
-        for (int md = 0; md < MD; ++md) *reinterpret_cast<f32x4*>(dst + 16 * md) = acc[md][nt];
+        for (int md = 0; md < MD; ++md) __builtin_nontemporal_store(acc[md][nt], reinterpret_cast<f32x4*>(dst + 16 * md));
     }
 }
 
