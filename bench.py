@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "verify-step us + achieved KV HBM GB/s (% peak), q8 E4M3 at 256K ctx"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published
+PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense FP16 matrix peak, AMD published
 KERNEL_SRC = os.path.join(ROOT, "paged_fp8_split_amd", "csrc", "pfs_kernels.hip")
 
 
@@ -71,6 +72,30 @@ def traffic_from_profiles(cfg: int):
     return t.get("bytes_per_launch")
 
 
+def sq_counters_from_profiles(cfg: int):
+    """Split-kernel SQ counter figures (profiles/sq_split_config<cfg>.json:
+    MFMA busy fraction per SIMD and the like), if those counters were taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"sq_split_config{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("derived")
+
+
+def split_mfma_flops(w) -> int:
+    """Dense matrix work of the split kernel: S = Q K^T and O = P V over every
+    live key, 2 flops per multiply-add, for the G x q rows of each KV head."""
+    import numpy as np
+
+    L = np.clip(w.live_len.astype(np.int64), 0, w.capacity)
+    rows = w.q * w.group
+    return int(L.sum()) * w.num_kv_heads * rows * w.head_dim * 2 * 2
+
+
 def split_algorithmic_bytes(w, plan) -> int:
     """Bytes the split kernel must move: live K+V, Q, the block-table entries of
     the live pages, and the FP32 partials (max, sum, D accumulators per row) of
@@ -85,6 +110,26 @@ def split_algorithmic_bytes(w, plan) -> int:
     splits = int((-(-L // plan.tokens_per_split)).sum())
     ws = splits * w.num_kv_heads * rows * (w.head_dim + 2) * 4
     return kv + qb + bt + ws
+
+
+def mfma_report(w, split_ms: float, cfg) -> dict:
+    """Matrix-core use of the split kernel: the dense FP16 work over the mean
+    launch time against the FP16 MFMA peak, and the MFMA-busy fraction that
+    the SQ counters measured on this kernel source for the default mode of
+    workload cfg (None if they are stale, or for cfg None)."""
+    flops = split_mfma_flops(w)
+    tf = flops / (split_ms * 1e-3) / 1e12
+    sq = (sq_counters_from_profiles(cfg) if cfg is not None else None) or {}
+    return {
+        "kernel": "pfs_split_kernel",
+        "flop_per_launch": flops,
+        "achieved": round(tf, 2),
+        "peak": PEAK_FP16_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tf / PEAK_FP16_MFMA_TFLOPS, 4),
+        "busy_frac_counters": sq.get("mfma_busy_frac"),
+        "valu_busy_frac_counters": sq.get("valu_busy_frac"),
+    }
 
 
 def codec_timing(w, t, dev, evict, reps: int = 20) -> dict:
@@ -243,6 +288,7 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
         "split_mean_launch_us": round(float(split_ms.mean()) * 1e3, 2),
         "split_achieved_GBps": round(ach, 2),
         "split_frac": round(ach / PEAK_HBM_GBS, 4),
+        "mfma": mfma_report(w, float(split_ms.mean()), None),
         "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
     }
     del t, ws, out
@@ -421,6 +467,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": split_bytes,
             "mean_launch_us": round(split_mean_ms * 1e3, 2),
         },
+        "mfma": mfma_report(w, split_mean_ms, args.config),
         "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
         "us_per_step_graph": round(float(graph_step_ms.mean()) * 1e3, 2),
         "graph_replay_cache_warm_us": round(graph_warm_ms * 1e3, 2),

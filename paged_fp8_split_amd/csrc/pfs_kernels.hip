@@ -169,6 +169,65 @@ struct SplitArgs {
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
+// Batches: the split grid takes the live units -- (request, KV head, split)
+// with split < ceil(L_b / tokens_per_split) -- in request, KV-head, split
+// order. Workgroups of empty splits would otherwise sit between live ones in
+// the dispatch order, and with the round-robin over the XCDs whole XCDs
+// would get only the late (mostly empty) splits of every request. Unit u of
+// the grid is the u-th live unit; false past the last one (uniform over the
+// workgroup). Every thread calls it. cnt: NT ints of LDS scratch, map: 3 ints
+// of LDS that stay untouched afterwards.
+template <int NT>
+__device__ bool live_unit(const SplitArgs& a, int unit, int32_t* cnt, int32_t* map, int& split, int& g, int& b) {
+    const int t = threadIdx.x;
+    const int per = (a.batch + NT - 1) / NT;  // requests per thread, a contiguous run
+    auto nsplit = [&](int bb) {
+        const int32_t L = clamp_i(a.live_len[bb], 0, a.capacity);
+        return (L + a.tokens_per_split - 1) / a.tokens_per_split;
+    };
+    int c = 0;
+    for (int k = 0; k < per; ++k)
+        if (t * per + k < a.batch) c += nsplit(t * per + k);
+    cnt[t] = c * a.num_kv_heads;
+    __syncthreads();
+    if (t < 64) {
+        constexpr int E = NT / 64;  // counts per lane
+        int s = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += cnt[t * E + e];
+        int incl = s;  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (t >= d) incl += y;
+        }
+        const int total = __shfl(incl, 63, 64);
+        const int excl = incl - s;
+        if (t == 0 && unit >= total) map[0] = -1;
+        if (unit >= excl && unit < incl) {  // exactly one lane
+            int rem = unit - excl;
+            int e = 0;
+            while (e < E - 1 && rem >= cnt[t * E + e]) rem -= cnt[t * E + e++];
+            const int bb_end = min(a.batch, (t * E + e + 1) * per);
+            int bb = (t * E + e) * per, n = 0;
+            for (; bb < bb_end; ++bb) {
+                n = nsplit(bb);
+                if (rem < n * a.num_kv_heads) break;
+                rem -= n * a.num_kv_heads;
+            }
+            const bool found = bb < bb_end && n > 0;
+            map[0] = found ? bb : -1;
+            map[1] = found ? rem / n : 0;
+            map[2] = found ? rem % n : 0;
+        }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(map[0]);
+    g = __builtin_amdgcn_readfirstlane(map[1]);
+    split = __builtin_amdgcn_readfirstlane(map[2]);
+    return b >= 0;
+}
+
 // Compile-time geometry of the split kernel: W = RG * TP waves (RG row groups
 // of RT 16-row tiles, TP token lanes), NS LDS stages of TP 32-token steps.
 template <int D, int RT, int RG, int TP, int NS>
@@ -265,6 +324,7 @@ pfs_split_kernel(const SplitArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t st6[NS > 4 ? SB : 16];
     __shared__ __attribute__((aligned(16))) uint8_t st7[NS > 4 ? SB : 16];
     __shared__ int64_t tile_off[pfs::kTileTableEntries];  // pool byte offset of every 16-token tile of the split
+    __shared__ int32_t unit_map[3];                        // (request, KV head, split) of a batch's live unit
     __shared__ float2 lds_ml[W][RT * 16];
     __shared__ __attribute__((aligned(16))) uint8_t merge_extra[C::MERGE_EXTRA_BYTES];
     auto stage = [&](auto kc) __attribute__((always_inline)) -> uint8_t* {
@@ -291,11 +351,16 @@ pfs_split_kernel(const SplitArgs a) {
     // request) get ids 8 apart and share that XCD's L2 for their K/V reads.
     const int x = blockIdx.x;
     const int rb = (x >> 3) % a.row_blocks;
-    const int unit = ((x >> 3) / a.row_blocks) * 8 + (x & 7);  // (split, KV head, request), split fastest
+    const int unit = ((x >> 3) / a.row_blocks) * 8 + (x & 7);  // (request, KV head, split), split fastest
     if (unit >= a.num_splits * a.num_kv_heads * a.batch) return;
-    const int split = unit % a.num_splits;
-    const int g = (unit / a.num_splits) % a.num_kv_heads;
-    const int b = unit / (a.num_splits * a.num_kv_heads);
+    int split, g, b;
+    if (a.batch == 1) {
+        split = unit % a.num_splits;
+        g = unit / a.num_splits;
+        b = 0;
+    } else if (!live_unit<64 * W>(a, unit, reinterpret_cast<int32_t*>(tile_off), unit_map, split, g, b)) {
+        return;  // past the last live unit
+    }
 
     const int32_t tok0 = split * a.tokens_per_split;
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
@@ -871,9 +936,10 @@ struct CombineArgs {
 // s % SL == t / (256 / SL) (its split lane), folded in ascending order CH at a
 // time (their loads are issued together) against a running maximum; the SL
 // split lanes of each column group are then merged in lane order against the
-// global maximum. Plans with at most CH splits use pfs_combine_rows_kernel.
+// global maximum. Plans with at most 4 CH splits use pfs_combine_rows_kernel.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChunk = 8;
+constexpr int kCombineRowSplits = 4 * kCombineChunk;  // the row kernel up to four rounds of loads
 
 template <int D, int SL>
 __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const CombineArgs a) {
@@ -965,9 +1031,10 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const Comb
 }
 
 
-// Few splits: one thread per 4 columns of one row folds every visible split
-// of that row itself (in ascending order, CH loads issued together, running
-// maximum) with no cross-lane merge; a workgroup covers 1024 / D whole rows.
+// Few splits (at most 4 CH): one thread per 4 columns of one row folds every
+// visible split of that row itself (in ascending order, CH loads issued
+// together, running maximum) with no cross-lane merge; a workgroup covers
+// 1024 / D whole rows.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void pfs_combine_rows_kernel(const CombineArgs a) {
     constexpr int CH = kCombineChunk;
@@ -1147,7 +1214,7 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.tokens_per_split = plan->tokens_per_split;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (plan->num_splits <= kCombineChunk) {  // every split of a row in one round of loads
+    if (plan->num_splits <= kCombineRowSplits) {  // each thread folds every split of its row
         const dim3 rgrid((plan->rows * p.head_dim / 4 + kCombineThreads - 1) / kCombineThreads, p.num_kv_heads,
                          p.batch);
         switch (p.head_dim) {
