@@ -331,6 +331,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="named workload (default 3: 256K context, q8)")
     ap.add_argument("--tokens-per-split", type=int, default=0)
+    ap.add_argument("--q", type=int, default=None,
+                    help="draft rows per request (the 8 x 64K batch also runs at q = 1 and q = 16)")
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,7 +367,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     note(f"generating workload config {args.config}")
-    w = W.config(args.config)
+    w = W.config(args.config, q=args.q)
     t = W.device_tensors(w, dev)
     plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
                          max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"],

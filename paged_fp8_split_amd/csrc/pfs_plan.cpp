@@ -151,6 +151,15 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
         if (splits < 1) splits = 1;
         tps = round_up((capacity + splits - 1) / splits, pfs::kPartitionTokens);
         const int64_t min_tps = 4 * (int64_t)pfs::kPartitionTokens;
+        // Batches: the plan cannot see the live lengths, and with one round
+        // of workgroups the longest requests' splits set the kernel time while
+        // the short ones' CUs idle. Capping a split at about 1 MiB of K+V
+        // bytes per KV head gives the dispatcher several rounds of small
+        // units to balance (a few % slower when every request is full).
+        if (p.batch > 1) {
+            const int64_t cap = ((int64_t)(1 << 20) / (2 * p.head_dim)) / pfs::kPartitionTokens * pfs::kPartitionTokens;
+            if (tps > cap) tps = cap;
+        }
         if (tps < min_tps) tps = min_tps;
         if (tps > max_tps) tps = max_tps;
     }

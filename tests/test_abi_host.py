@@ -56,6 +56,28 @@ BASE = dict(batch=1, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_siz
             head_map=[h // 8 for h in range(16)])
 
 
+def test_default_split_single_request_is_one_round():
+    """One request: the default split fills one round of workgroups (256 CUs,
+    one per CU at head_dim 256): 4096 pages x 64 tokens over 2 KV heads ->
+    128 splits of 2048 tokens."""
+    p = _lib.Plan(**BASE)
+    assert (p.tokens_per_split, p.num_splits) == (2048, 128)
+
+
+@pytest.mark.parametrize("head_dim,cap", [(256, 2048), (128, 4096), (64, 8192)])
+def test_default_split_batches_are_capped_near_one_mib(head_dim, cap):
+    """Batches: the default split holds at most about 1 MiB of K+V bytes per
+    KV head (cap tokens x 2 x head_dim bytes), so that splits of unequal
+    requests can be balanced by the dispatcher; one round would give larger
+    splits here (batch 32 x 2 KV heads at 32768 tokens: 8192)."""
+    kw = dict(BASE, batch=32, head_dim=head_dim, max_pages_per_row=512, kv_page_stride=64 * 2 * head_dim,
+              kv_token_stride=2 * head_dim, kv_head_stride=head_dim)
+    p = _lib.Plan(**kw)
+    assert p.tokens_per_split == cap
+    assert p.tokens_per_split * 2 * head_dim <= 1 << 20
+    assert p.num_splits == 32768 // cap
+
+
 def plan_status(**over):
     kw = dict(BASE)
     kw.update(over)
