@@ -1098,9 +1098,9 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_rows_kernel(const
     for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((acc[c] * vs) / lw);
 }
 
-template <int D, int RT, int RG, int FMT, bool RES>
+template <int D, int RT, int RG, int FMT, bool RES, bool NARROW = false>
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
-    constexpr int W = pfs::split_waves(D, RG);
+    constexpr int W = pfs::split_waves(D, RG, NARROW);
     constexpr int TP = W / RG;
     constexpr int NS = pfs::split_stages(D, TP, W);
     const int64_t units = (int64_t)a.num_splits * a.num_kv_heads * a.batch;
@@ -1111,37 +1111,43 @@ hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
 }
 
 // Row groups above one occur only with the most row tiles a wave can hold.
+// The plan's wave count must be the one the kernel template derives.
 template <int D, int RT, int FMT, bool RES>
-hipError_t launch_split_rt(const SplitArgs& a, int32_t row_groups, hipStream_t stream) {
+hipError_t launch_split_rt(const SplitArgs& a, int32_t row_groups, int32_t waves, hipStream_t stream) {
     if constexpr (RT > pfs::max_row_tiles(D)) {
         return hipErrorInvalidValue;
     } else {
-        if (row_groups == 1) return launch_split<D, RT, 1, FMT, RES>(a, stream);
+        if (row_groups == 1 && waves == pfs::split_waves(D, 1)) return launch_split<D, RT, 1, FMT, RES>(a, stream);
         if constexpr (RT == pfs::max_row_tiles(D)) {
-            if (row_groups == 2) return launch_split<D, RT, 2, FMT, RES>(a, stream);
-            if (row_groups == 4) return launch_split<D, RT, 4, FMT, RES>(a, stream);
+            if (row_groups == 2 && waves == pfs::split_waves(D, 2)) return launch_split<D, RT, 2, FMT, RES>(a, stream);
+            if (row_groups == 4 && waves == pfs::split_waves(D, 4)) return launch_split<D, RT, 4, FMT, RES>(a, stream);
+            if constexpr (pfs::split_narrow(D, 4, 2)) {
+                if (row_groups == 4 && waves == pfs::split_waves(D, 4, true))
+                    return launch_split<D, RT, 4, FMT, RES, true>(a, stream);
+            }
         }
         return hipErrorInvalidValue;
     }
 }
 
 template <int D, int FMT, bool RES>
-hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t row_groups, hipStream_t stream) {
+hipError_t launch_split_d(const SplitArgs& a, int32_t row_tiles, int32_t row_groups, int32_t waves,
+                          hipStream_t stream) {
     switch (row_tiles) {
-        case 1: return launch_split_rt<D, 1, FMT, RES>(a, row_groups, stream);
-        case 2: return launch_split_rt<D, 2, FMT, RES>(a, row_groups, stream);
-        case 4: return launch_split_rt<D, 4, FMT, RES>(a, row_groups, stream);
+        case 1: return launch_split_rt<D, 1, FMT, RES>(a, row_groups, waves, stream);
+        case 2: return launch_split_rt<D, 2, FMT, RES>(a, row_groups, waves, stream);
+        case 4: return launch_split_rt<D, 4, FMT, RES>(a, row_groups, waves, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int FMT, bool RES>
 hipError_t launch_split_fmt(const SplitArgs& a, int32_t head_dim, int32_t row_tiles, int32_t row_groups,
-                            hipStream_t stream) {
+                            int32_t waves, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_split_d<64, FMT, RES>(a, row_tiles, row_groups, stream);
-        case 128: return launch_split_d<128, FMT, RES>(a, row_tiles, row_groups, stream);
-        case 256: return launch_split_d<256, FMT, RES>(a, row_tiles, row_groups, stream);
+        case 64: return launch_split_d<64, FMT, RES>(a, row_tiles, row_groups, waves, stream);
+        case 128: return launch_split_d<128, FMT, RES>(a, row_tiles, row_groups, waves, stream);
+        case 256: return launch_split_d<256, FMT, RES>(a, row_tiles, row_groups, waves, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1185,11 +1191,11 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     hipError_t e;
     // the residual probabilities exist for E4M3 only (the plan rejects E5M2 with them)
     if (p.kv_format == PFS_KV_E4M3 && p.pv_residual)
-        e = launch_split_fmt<PFS_KV_E4M3, true>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+        e = launch_split_fmt<PFS_KV_E4M3, true>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
     else if (p.kv_format == PFS_KV_E4M3)
-        e = launch_split_fmt<PFS_KV_E4M3, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+        e = launch_split_fmt<PFS_KV_E4M3, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
     else if (p.kv_format == PFS_KV_E5M2 && !p.pv_residual)
-        e = launch_split_fmt<PFS_KV_E5M2, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, s);
+        e = launch_split_fmt<PFS_KV_E5M2, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
     else
         return PFS_ERR_UNSUPPORTED;
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;

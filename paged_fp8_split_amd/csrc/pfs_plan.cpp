@@ -26,7 +26,7 @@ int32_t pow2_ceil(int32_t v) {
 // 32-token steps (token lanes). Tiles per wave come first: every wave converts
 // the E4M3 bytes it reads, so more rows per wave means fewer conversions per
 // row. Rows beyond RT * RG tiles become row blocks of the grid.
-void choose_split_shape(int32_t rows, int32_t head_dim, pfs_plan* plan) {
+void choose_split_shape(int32_t rows, int32_t head_dim, int32_t batch, pfs_plan* plan) {
     const int32_t tiles = (rows + 15) / 16 > 0 ? (rows + 15) / 16 : 1;
     const int32_t max_rt = pfs::max_row_tiles(head_dim);
     const int32_t rt = pow2_ceil(tiles) < max_rt ? pow2_ceil(tiles) : max_rt;
@@ -34,7 +34,7 @@ void choose_split_shape(int32_t rows, int32_t head_dim, pfs_plan* plan) {
     const int32_t rg = groups < 4 ? groups : 4;
     plan->row_tiles = rt;
     plan->row_groups = rg;
-    plan->waves = pfs::split_waves(head_dim, rg);
+    plan->waves = pfs::split_waves(head_dim, rg, pfs::split_narrow(head_dim, rg, batch));
     plan->token_lanes = plan->waves / rg;
     plan->row_blocks = (tiles + rt * rg - 1) / (rt * rg);
 }
@@ -132,7 +132,7 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
             plan->qhead[g * G + fill[g]++] = (uint8_t)h;
         }
     }
-    choose_split_shape(plan->rows, p.head_dim, plan);
+    choose_split_shape(plan->rows, p.head_dim, p.batch, plan);
 
     // Split length: a pure function of the shape (never of device data), so a
     // plan always folds the same partitions in the same order.
