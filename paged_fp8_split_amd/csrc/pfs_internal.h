@@ -24,13 +24,14 @@ constexpr int kCUs = 256;  // MI355X compute units
 // times TP token lanes; a stage holds TP 32-token steps of K and V bytes.
 constexpr int split_stage_bytes(int head_dim, int token_lanes) { return token_lanes * 64 * head_dim; }
 // Eight waves whenever a stage of 8 / RG steps stays within 64 KB. Batches
-// at head_dim 256 with four row groups take four waves instead (one token
-// lane, 16 KB stages), so that two workgroups share a CU: one's pipeline fill
-// and partial write overlap the other's stream while the dispatcher balances
-// requests of unequal length (one request keeps eight waves: its splits all
-// have the same length, and two per CU would double its partials).
+// with four row groups at head_dim 128 or 256 take four waves instead (one
+// token lane, stages of 8 or 16 KB), so that two workgroups share a CU: one's
+// pipeline fill and partial write overlap the other's stream while the
+// dispatcher balances requests of unequal length. One request keeps eight
+// waves: its splits all have the same length, and two per CU would double
+// its partials. (Two row groups at head_dim 128 measured no gain.)
 constexpr bool split_narrow(int head_dim, int row_groups, int batch) {
-    return batch > 1 && head_dim >= 256 && row_groups == 4;
+    return batch > 1 && head_dim >= 128 && row_groups == 4;
 }
 constexpr int split_waves(int head_dim, int row_groups, bool narrow = false) {
     return narrow ? 4 : (split_stage_bytes(head_dim, 8 / row_groups) <= 65536 ? 8 : 4);
