@@ -68,6 +68,11 @@ SMALL = [
                                    lengths=[600]), 256),
     ("d256-q16-g8-rowblocks", dict(batch=1, q=16, num_q_heads=8, num_kv_heads=1, head_dim=256, page_size=64,
                                    lengths=[700]), 256),
+    # batches with four row groups run four-wave workgroups, two per CU
+    ("d256-q16-g8-batch-rowblocks", dict(batch=3, q=16, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                                         lengths=[2500, 0, 777]), 0),
+    ("d128-q16-g8-batch-ragged", dict(batch=4, q=16, num_q_heads=32, num_kv_heads=4, head_dim=128, page_size=64,
+                                      lengths=[5000, 64, 1, 3000]), 0),
     ("d128-q5-g6-padded", dict(batch=2, q=5, num_q_heads=12, num_kv_heads=2, head_dim=128, page_size=48,
                                lengths=[400, 90], token_pad=16, page_pad=64), 0),
     ("d64-outliers-pow2", dict(batch=2, q=8, num_q_heads=8, num_kv_heads=4, head_dim=64, page_size=16,
