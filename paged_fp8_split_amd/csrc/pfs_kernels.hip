@@ -362,6 +362,7 @@ pfs_split_kernel(const SplitArgs a) {
         return;  // past the last live unit
     }
 
+    const int r_wave = rb * (RG * RT * 16) + rg * (RT * 16);  // first row of this wave
     const int32_t tok0 = split * a.tokens_per_split;
     const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
     // the first block-table entry this thread resolves, read before the live
@@ -369,47 +370,61 @@ pfs_split_kernel(const SplitArgs a) {
     // two reads overlap
     const int32_t t_first = tok0 + 16 * (int)threadIdx.x;
     const int32_t pg_first = t_first / a.page_size;
-    const int32_t page_first = (t_first < a.capacity && 16 * (int)threadIdx.x < a.tokens_per_split) ? bt_row[pg_first] : 0;
-    const int32_t L = __builtin_amdgcn_readfirstlane(clamp_i(a.live_len[b], 0, a.capacity));
-    if (tok0 >= L) return;  // nothing live in this split: the combine never reads it
+    // (read unconditionally, at an index clamped into the row, and selected at
+    // its use: a load under a branch is waited for where the branch joins)
+    const int32_t page_any = bt_row[min(pg_first, a.max_pages - 1)];
+    // The live length is read with a vector load (through an opaque zero
+    // index): vector loads return in order, so the kernel waits for it and the
+    // block-table entry together without also waiting for the Q reads below.
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    const int32_t L_raw = a.live_len[b + vzero];
+    const float kscale_g = a.kscale[g];
+    // ---- Q^T operands in registers: (nt, ks) holds row r_wave + 16 nt + lc,
+    //      dims 64(ks/2) + 16 lg + 8(ks&1) + [0, 8). Issued before the
+    //      live length is known: their cold reads overlap the live-length and
+    //      block-table reads instead of following them. ----
+    // Padding rows (r >= rows) read row 0 here, with no branch around the
+    // loads, and are zeroed after the first K/V loads are issued.
+    f16x8 qop[RT][KSTEPS];
+#pragma unroll
+    for (int nt = 0; nt < RT; ++nt) {
+        const int r = r_wave + nt * 16 + lc;
+        const int rr = r < a.rows ? r : 0;
+        const int i = rr / a.group;
+        const int h = a.qhead[g * a.group + (rr % a.group)];
+        const _Float16* qrow = a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D;
+#pragma unroll
+        for (int j = 0; j < KSTEPS / 2; ++j) {
+            qop[nt][2 * j] = bit_cast_<f16x8>(*reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg));
+            qop[nt][2 * j + 1] = bit_cast_<f16x8>(*reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg + 8));
+        }
+    }
+
+    const int32_t L = __builtin_amdgcn_readfirstlane(clamp_i(L_raw, 0, a.capacity));
+    const int32_t page_first = (t_first < a.capacity && 16 * (int)threadIdx.x < a.tokens_per_split) ? page_any : 0;
+    // A split with nothing live (tok0 >= L; only single requests shorter than
+    // the capacity have them) runs on with no steps and zero-size loads and
+    // returns before its partial write: the combine never reads it. (An early
+    // return here would let the compiler move the Q reads behind it.)
+    const bool live_split = tok0 < L;
     const int32_t tok_end = min(tok0 + a.tokens_per_split, L);
     const int32_t nsteps = (tok_end - tok0 + kStep - 1) / kStep;
     const int32_t nstages = (nsteps + TP - 1) / TP;
-    const int r_wave = rb * (RG * RT * 16) + rg * (RT * 16);  // first row of this wave
 
     // ---- tile table: pool byte offset of every 16-token tile of the split ----
     {
         const int64_t head_off = (int64_t)g * a.head_stride;
         const int32_t ntiles = min((tok_end - tok0 + 15) / 16, pfs::kTileTableEntries);
-        for (int e = threadIdx.x; e < ntiles; e += 64 * W) {
+        auto put = [&](int e, int32_t page) __attribute__((always_inline)) {
             const int32_t t0 = tok0 + 16 * e;
-            const int32_t pg = t0 / a.page_size;
-            const int32_t slot = t0 - pg * a.page_size;
-            const int32_t page = e == (int)threadIdx.x ? page_first : bt_row[pg];
+            const int32_t slot = t0 - (t0 / a.page_size) * a.page_size;
             tile_off[e] = (int64_t)page * a.page_stride + (int64_t)slot * a.token_stride + head_off;
-        }
-    }
-
-    // ---- Q^T operands in registers: (nt, ks) holds row r_wave + 16 nt + lc,
-    //      dims 64(ks/2) + 16 lg + 8(ks&1) + [0, 8) ----
-    f16x8 qop[RT][KSTEPS];
-#pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-        const int r = r_wave + nt * 16 + lc;
-        const bool real = r < a.rows;
-        const int i = real ? r / a.group : 0;
-        const int h = real ? a.qhead[g * a.group + (r % a.group)] : 0;
-        const _Float16* qrow = a.qptr + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D;
-#pragma unroll
-        for (int j = 0; j < KSTEPS / 2; ++j) {
-            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (real) {
-                lo = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg);
-                hi = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * lg + 8);
-            }
-            qop[nt][2 * j] = bit_cast_<f16x8>(lo);
-            qop[nt][2 * j + 1] = bit_cast_<f16x8>(hi);
-        }
+        };
+        // the first entry of each thread, from the entry read above, outside
+        // any loop (so that waiting for it does not wait for the Q reads)
+        if ((int)threadIdx.x < ntiles) put(threadIdx.x, page_first);
+        for (int e = threadIdx.x + 64 * W; e < ntiles; e += 64 * W) put(e, bt_row[(tok0 + 16 * e) / a.page_size]);
     }
 
     // causal limit of this lane's row in each row tile: keys [0, lim) are visible.
@@ -422,14 +437,7 @@ pfs_split_kernel(const SplitArgs a) {
         lim[nt] = (r < a.rows) ? clamp_i((int64_t)L - a.q + r / a.group + 1, 0, L) : L;
     }
     const int32_t lim_lo = clamp_i((int64_t)L - a.q + 1, 0, L);  // smallest limit of any real row
-    float cscale = a.sm_scale_log2e * a.kscale[g];  // score scale, log2 domain
-    if (cscale < 0.0f) {  // keep the scale non-negative: max(s) * c is then the max of the scaled scores
-        cscale = -cscale;
-#pragma unroll
-        for (int nt = 0; nt < RT; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qop[nt][ks] = -qop[nt][ks];
-    }
+    float cscale = a.sm_scale_log2e * kscale_g;  // score scale, log2 domain
 
     f32x4 acc[MD][RT];
     f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
@@ -734,6 +742,22 @@ pfs_split_kernel(const SplitArgs a) {
     constexpr bool PIPE = NS >= 4;
     static_for<NS - 1>([&](auto kc) __attribute__((always_inline)) { fire(prep(decltype(kc)::value), stage(kc)); });
     Pending pend = prep(NS - 1);  // loads of the next stage to issue
+    // (after the first loads are issued: these wait for Q only when there are
+    // padding rows or the scale is negative)
+    if (r_wave + 16 * RT > a.rows) {
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt)
+            if (r_wave + nt * 16 + lc >= a.rows)
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) qop[nt][ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if (cscale < 0.0f) {  // keep the scale non-negative: max(s) * c is then the max of the scaled scores
+        cscale = -cscale;
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) qop[nt][ks] = -qop[nt][ks];
+    }
     if constexpr (PIPE) {
         // ---- NS - 2 stages in flight ahead of the one whose QK is folded ----
         Scores sc_cur;
@@ -898,6 +922,7 @@ pfs_split_kernel(const SplitArgs a) {
         if (tl != 0) return;
     }
 
+    if (!live_split) return;
     // ---- emit the split partial: (reference max, sum) and the unnormalized PV
     // (non-temporal stores: the combine reads them once, from beyond the L2) ----
     // accumulator element i of d tile md is column 16 md + 4 lg + i of row r
