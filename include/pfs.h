@@ -112,7 +112,13 @@ typedef struct pfs_problem {
     int32_t max_pages_per_row;  /* block-table row length (capacity = this * page_size) */
     int32_t num_pool_pages;     /* physical pages in each pool */
     int32_t partition_tokens;   /* 64 (the only partition size this build runs) */
-    int32_t tokens_per_split;   /* 0 = library default; else a multiple of partition_tokens */
+    int32_t tokens_per_split;   /* 0 = library default: a function of the shape only, the
+                                   smallest multiple of 64 (at least 256) for which one
+                                   round of split workgroups fills the GPU, capped for
+                                   batch > 1 at 2^20 / (2 * head_dim) tokens (about 1 MiB
+                                   of K+V per request and KV head) so that requests of
+                                   unequal live length can be balanced; else a multiple
+                                   of partition_tokens, at most 16384 */
     int32_t kv_format;          /* PFS_KV_E4M3 (0) or PFS_KV_E5M2 (1): how the pool bytes decode */
     int32_t pv_residual;        /* 0: P enters PV as one FP16 operand; 1: as an FP16 high part
                                    plus an FP16 residual (see below); E4M3 only */
