@@ -113,8 +113,9 @@ typedef struct pfs_problem {
     int32_t num_pool_pages;     /* physical pages in each pool */
     int32_t partition_tokens;   /* 64 (the only partition size this build runs) */
     int32_t tokens_per_split;   /* 0 = library default: a function of the shape only, the
-                                   smallest multiple of 64 (at least 256) for which one
-                                   round of split workgroups fills the GPU, capped for
+                                   smallest multiple of 64 (at least 256, at most the
+                                   capacity rounded up to 64) for which one round of
+                                   split workgroups fills the GPU, capped for
                                    batch > 1 at 2^20 / (2 * head_dim) tokens (about 1 MiB
                                    of K+V per request and KV head) so that requests of
                                    unequal live length can be balanced; else a multiple
