@@ -62,3 +62,28 @@ def test_random_shape_parity(k):
         for i in range(w.q):
             if L[bb] - w.q + i + 1 <= 0:
                 assert np.all(a[bb, i].view(np.uint16) == 0), f"request {bb} row {i}"
+
+
+MEDIUM = [
+    # (batch, q, Hq, Hkv, head_dim, page, lengths, capacity): default plans, batch cap and
+    # four-wave batch workgroups with several splits per request
+    (4, 8, 16, 2, 256, 64, [40000, 2048, 0, 20481], 40960),
+    (3, 16, 32, 4, 128, 64, [16385, 30000, 4095], 32768),
+    (6, 1, 32, 4, 128, 32, [9000, 1, 12345, 0, 7, 20000], 20480),
+    (2, 5, 12, 2, 256, 48, [33333, 48], 36000),
+    (1, 8, 16, 2, 256, 64, [9000], 65536),   # one request far below its capacity: empty splits
+    (5, 3, 8, 1, 64, 16, [25000, 100, 3, 17000, 8191], 25600),
+]
+
+
+@pytest.mark.parametrize("k", range(len(MEDIUM)))
+def test_medium_batch_parity_default_plan(k):
+    batch, q, hq, hkv, D, page, lengths, cap = MEDIUM[k]
+    w = W.build(seed=800 + k, batch=batch, q=q, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=page,
+                lengths=lengths, capacity=cap, outlier_frac=0.01)
+    log(f"[medium {k}] B={batch} q={q} Hq={hq} Hkv={hkv} D={D} page={page} L={lengths} cap={cap}")
+    out, t = run(w)
+    a = to_np(out)
+    b = to_np(run(w, tensors=t)[0])
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), "repeat launch differs"
+    judge(a, oracle_ref(w), f"medium {k}")
