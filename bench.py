@@ -7,18 +7,19 @@ E4M3 K/V with per-head scales and 1% outlier tokens, page size 64 (the
 256K-context q8 case the metric is quoted on). Inputs are synthetic, seeded and
 resident in HBM before the timed region starts.
 
-Timing: W untimed warmup steps, then K timed steps (split and combine
-launched back to back). Before every step an untimed read of a clean 1 GiB
-buffer evicts the 256 MB Infinity Cache and the L2s, so the KV bytes come from
-HBM. The scrub only reads: a scrub that writes leaves dirty lines whose
-write-back then competes with the timed kernel's reads. Each step is
-bracketed by HIP events recorded on the stream the kernels run on, and the
-whole timed loop by a device synchronize. A second pass puts an event between
-the kernels as well (e0 -> e1 -> e2) for the per-kernel figures: the split
-kernel's mean launch time is the roofline's denominator. That middle event
-delays the combine's start by a few microseconds, which is why the step is
-timed without it. A third pass replays the step captured as one HIP graph
-(reported beside the main figure).
+Timing follows the pages' protocol of graph-replayed operator timing ("[Bugfix]
+Use FP32 state and E4M3 defaults for DFlash2", Test Plan and Results: 20
+warmups, then timed replays): the step (split and combine) is captured once
+as a HIP graph, W untimed warmup replays run, then K timed replays. Before
+every replay an untimed read of a clean 1 GiB buffer evicts the 256 MB
+Infinity Cache and the L2s, so the KV bytes come from HBM. The scrub only
+reads: a scrub that writes leaves dirty lines whose write-back then competes
+with the timed kernel's reads. Each replay is bracketed by HIP events on the
+stream the graph is launched on. `value`, `ms_per_step` and
+`kv_pct_of_peak_hbm` are those replays. The same step launched eagerly (the
+two kernels back to back, events around the step) is reported beside it, and
+a further eager pass with an event between the kernels gives the per-kernel
+figures: the split kernel's mean launch time is the roofline's denominator.
 
 Prints one JSON line. `value` is the achieved KV read rate: live K+V bytes of
 the step divided by the mean step time.
@@ -129,6 +130,8 @@ def mfma_report(w, split_ms: float, cfg) -> dict:
         "frac": round(tf / PEAK_FP16_MFMA_TFLOPS, 4),
         "busy_frac_counters": sq.get("mfma_busy_frac"),
         "valu_busy_frac_counters": sq.get("valu_busy_frac"),
+        "counters_source": (f"rocprofv3 --pmc SQ counters of this kernel source, read from "
+                            f"profiles/sq_split_config{cfg}.json (not measured in this run)") if sq else None,
     }
 
 
@@ -253,11 +256,11 @@ def time_graph(graph, evict, stream, steps: int, warmup: int):
     return np.array([e[0].elapsed_time(e[1]) for e in evs]), wall
 
 
-def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3", pv_residual: bool = False,
-            w=None) -> dict:
-    """The workload in another mode of the path (E5M2 bytes, or high/residual
-    FP16 probabilities): step and split-kernel times, measured like the main
-    line."""
+def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3",
+            pv_mode: str = "high_residual", w=None) -> dict:
+    """The workload in another mode of the path (E5M2 bytes, or the opt-in
+    single FP16 probability operand): step and split-kernel times, measured
+    eagerly like the main line's per-kernel pass."""
     import torch
 
     import paged_fp8_split_amd as pfs
@@ -270,7 +273,7 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
     t = W.device_tensors(w, dev)
     plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
                          max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"], kv_format=kv_format,
-                         pv_residual=pv_residual)
+                         pv_mode=pv_mode)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
@@ -282,7 +285,7 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
     sb = split_algorithmic_bytes(w, plan)
     ach = sb / (float(split_ms.mean()) * 1e-3) / 1e9
     res = {
-        "workload": w.name + ("-e5m2" if kv_format == "e5m2" else "") + ("-pv-residual" if pv_residual else ""),
+        "workload": w.name + ("-e5m2" if kv_format == "e5m2" else "") + ("-pv-fp16" if pv_mode == "fp16" else ""),
         "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
         "kv_GBps": round(w.kv_bytes() / (float(step_ms.mean()) * 1e-3) / 1e9, 2),
         "split_mean_launch_us": round(float(split_ms.mean()) * 1e3, 2),
@@ -296,24 +299,49 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
     return res
 
 
-def cpu_baseline(w, seconds: float) -> dict:
-    """The FP64 oracle, as it stands, on the host cores: whole verify steps of
-    the same workload, repeated until `seconds` have elapsed (at least one)."""
-    import oracle
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
 
-    threads = oracle.max_threads()
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, cfg_of_w: int, seconds: float, single_thread_configs=(1, 3)):
+    """The FP64 oracle, as it stands, on the host cores: whole verify steps of
+    the same workload with one OpenMP thread per core this process may run on,
+    repeated until `seconds` have elapsed (at least one step); then one
+    single-thread step of each named workload in `single_thread_configs`.
+    Returns (report, oracle result of the timed workload)."""
+    import oracle
+    from paged_fp8_split_amd import workloads as W
+
+    threads = len(os.sched_getaffinity(0))
     units = w.batch * w.num_q_heads * w.q
     t0 = time.perf_counter()
     reps = 0
     while True:
-        oracle.verify(w)
+        ref = oracle.verify(w, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         note(f"cpu oracle step {reps}: {el:.1f} s elapsed")
         if el >= seconds:
             break
     per_step = el / reps
-    return {
+    single = {}
+    for cfg in single_thread_configs:
+        wc = w if cfg == cfg_of_w else W.config(cfg)
+        t1 = time.perf_counter()
+        oracle.verify(wc, threads=1)
+        dt = time.perf_counter() - t1
+        note(f"cpu oracle, one thread, {wc.name}: {dt:.2f} s")
+        single[wc.name] = round(dt, 4)
+    rep = {
         "value": round(w.kv_bytes() / per_step / 1e9, 4),
         "unit": "GB/s",
         "cores": int(min(threads, units)),
@@ -321,6 +349,32 @@ def cpu_baseline(w, seconds: float) -> dict:
         "sample": f"{reps} whole verify step(s) of the timed workload ({w.name}), FP64, "
                   f"{per_step:.2f} s per step",
         "seconds_per_step": round(per_step, 4),
+        "threads": threads,
+        "cpu_model": cpu_model(),
+        "single_thread_seconds_per_step": single,
+    }
+    return rep, ref
+
+
+def parity_report(y16, r) -> dict:
+    """The timed output against the oracle: relative L2, max abs per band of
+    |r|, and the pages' count of FP16 outputs that differ from the oracle
+    result rounded to FP16 ("[Kernel][SM70] Add opt-in E4M3 grouped attention
+    with FP32 partials", test plan and results)."""
+    import numpy as np
+
+    y = y16.astype(np.float64)
+    err = np.abs(y - r)
+    ar = np.abs(r)
+    bands = {}
+    for lo, hi in ((0.0, 8.0), (8.0, 16.0), (16.0, float("inf"))):
+        m = (ar >= lo) & (ar < hi)
+        bands[f"[{lo:g},{hi:g})"] = round(float(err[m].max()), 6) if m.any() else None
+    return {
+        "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(r)),
+        "max_abs_by_band": bands,
+        "fp16_disagreements": int((y16.view(np.uint16) != r.astype(np.float16).view(np.uint16)).sum()),
+        "elements": int(r.size),
     }
 
 
@@ -390,26 +444,26 @@ def main() -> int:
     def combine():
         _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
 
-    note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B")
-    # the timed steps: split and combine launched back to back, HIP events
-    # around each step on the kernels' stream
-    _, _, step_ms, wall = time_steps(split, combine, evict, stream, args.steps, args.warmup, mid_event=False)
-    y = out.cpu().numpy()
-    out_sha = hashlib.sha256(y.tobytes()).hexdigest()
-    # per-kernel figures: a second pass with an event between the kernels (the
-    # split kernel's launch time is the roofline's denominator)
-    split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, args.steps, 0, mid_event=True)
-
-    # the same step captured as one HIP graph, each replay after the scrub
+    note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B, "
+         f"{plan.num_cus} CUs")
+    # the headline: the step captured once as a HIP graph, replayed after each scrub
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         _lib.verify(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
                     t["live_len"], out, ws)
     torch.cuda.synchronize()
-    graph_step_ms, _ = time_graph(g, evict, stream, args.steps, 3)
-    same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
+    note("graph captured; timing replays")
+    graph_step_ms, wall = time_graph(g, evict, stream, args.steps, args.warmup)
+    y = out.cpu().numpy()
+    out_sha = hashlib.sha256(y.tobytes()).hexdigest()
+    # the same step launched eagerly, kernels back to back
+    _, _, step_ms, _ = time_steps(split, combine, evict, stream, args.steps, 3, mid_event=False)
+    eager_same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
+    # per-kernel figures: an eager pass with an event between the kernels (the
+    # split kernel's launch time is the roofline's denominator)
+    split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, args.steps, 0, mid_event=True)
 
-    # the same graph replayed back to back without scrubs (cache-warm: context only)
+    # the graph replayed back to back without scrubs (cache-warm: context only)
     ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 50
     ga.record()
@@ -420,7 +474,8 @@ def main() -> int:
     graph_warm_ms = ga.elapsed_time(gb) / reps
 
     kv = w.kv_bytes()
-    mean_ms = float(step_ms.mean())
+    mean_ms = float(graph_step_ms.mean())
+    eager_ms = float(step_ms.mean())
     value = kv / (mean_ms * 1e-3) / 1e9
     split_bytes = split_algorithmic_bytes(w, plan)
     split_mean_ms = float(split_ms.mean())
@@ -435,13 +490,15 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(mean_ms, 5),
         "us_per_step": round(mean_ms * 1e3, 2),
-        "us_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(graph_step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "kv_pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "timing": "HIP-graph replay of split + combine, events around each replay, Infinity Cache scrubbed before each",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "precision": "E4M3 KV bytes, FP16 MFMA operands, FP32 accumulation and split partials, FP16 output",
+        "precision": "E4M3 KV bytes; FP16 MFMA operands (probabilities as FP16 high + FP16 residual); FP32 "
+                     "accumulation and split partials; FP16 output",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -455,6 +512,8 @@ def main() -> int:
             "partition_tokens": 64,
             "tokens_per_split": plan.tokens_per_split,
             "num_splits": plan.num_splits,
+            "num_cus": plan.num_cus,
+            "pv_mode": "high_residual",
             "kv_bytes": kv,
             "infinity_cache_scrub": scrub is not None,
         },
@@ -466,14 +525,18 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
+            "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this kernel source, read from "
+                               f"profiles/traffic_split_config{args.config}.json (not measured in this run)")
+            if traffic is not None else None,
             "algorithmic_bytes_per_launch": split_bytes,
             "mean_launch_us": round(split_mean_ms * 1e3, 2),
         },
         "mfma": mfma_report(w, split_mean_ms, args.config),
+        "us_per_step_eager": round(eager_ms * 1e3, 2),
+        "kv_pct_of_peak_hbm_eager": round(100.0 * kv / (eager_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "eager_output_matches_graph": bool(eager_same),
         "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
-        "us_per_step_graph": round(float(graph_step_ms.mean()) * 1e3, 2),
         "graph_replay_cache_warm_us": round(graph_warm_ms * 1e3, 2),
-        "graph_output_matches_eager": bool(same),
         "timed_loop_wall_s": round(wall, 4),
         "output_sha256": out_sha,
         "kernel_source_sha": kernel_source_sha(),
@@ -483,12 +546,13 @@ def main() -> int:
     if not args.no_variants:
         vs, vw = max(args.steps // 2, 10), max(args.warmup // 2, 3)
         res["variants"] = {
-            "pv_residual": variant(args.config, dev, evict, vs, vw, pv_residual=True, w=w),
+            "pv_fp16": variant(args.config, dev, evict, vs, vw, pv_mode="fp16", w=w),
             "e5m2": variant(args.config, dev, evict, vs, vw, kv_format="e5m2"),
         }
     if not args.no_cpu_baseline:
         note("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"], ref = cpu_baseline(w, args.config, args.cpu_seconds)
+        res["parity_vs_oracle"] = parity_report(y, ref)
     print(json.dumps(res), flush=True)
     return 0
 

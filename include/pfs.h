@@ -22,9 +22,10 @@
  *   audited TP2 DFlash2 31/29 ms endpoint", Purpose: K64 partition order).
  *   Every split emits an FP32 running max, an FP32 sum and an unnormalized
  *   FP32 PV accumulator into the caller's workspace; a combine pass rescales
- *   the splits, reduces them in ascending split order, normalizes and rounds
- *   once ("... FP32 partials", revision 3 bullet: max/sum and unnormalized PV
- *   kept in FP32 until one final combine).
+ *   the splits, reduces them in a fixed order (stated at pfs_verify_combine),
+ *   normalizes and rounds once ("[Kernel][SM70] Add opt-in E4M3 grouped
+ *   attention with FP32 partials", final status, revision 3 bullet: max/sum
+ *   and unnormalized PV kept in FP32 until one final combine).
  *
  * Every call returns a status code (PFS_OK == 0, errors < 0); no exception and
  * no fallback path crosses this boundary: an unsupported shape is an error.
@@ -45,7 +46,7 @@ extern "C" {
  * changes. Callers refuse a library whose pfs_abi_version() differs from the
  * header they were built against (the pages' "stale native rejection":
  * "[Bugfix] Use FP32 state ...", Purpose, precision revision / rebuild). */
-#define PFS_ABI_VERSION 4
+#define PFS_ABI_VERSION 5
 
 enum {
     PFS_OK = 0,
@@ -71,16 +72,21 @@ enum {
  * scales, layout and the rest of the arithmetic are the same. */
 enum { PFS_KV_E4M3 = 0, PFS_KV_E5M2 = 1 };
 
-/* High/residual probabilities (pfs_problem.pv_residual = 1; "[Kernel][SM70]
- * Add opt-in E4M3 grouped attention with FP32 partials", historical scope:
- * the PV probability as high/residual FP16 operands, the residual scaled by
- * 2048 against an exactly representable inverse scale on E4M3-derived V).
- * Each probability p (FP32) enters the PV product as hi = RNE_fp16(p) and
- * res = RNE_fp16((p - hi) * 2048); the kernel adds hi * V + res * (V / 2048),
- * where V / 2048 is exact in FP16 for every E4M3 value, and the row sums get
- * hi + res / 2048 likewise. The FP16 rounding of P then costs about 2^-22
- * instead of 2^-12 relative; the PV matrix work doubles. Not defined for
- * E5M2 pools (V / 2048 is not exact there): PFS_ERR_UNSUPPORTED. */
+/* How each probability p enters the PV product (pfs_problem.pv_mode).
+ * PFS_PV_HIGH_RESIDUAL (0, the default) carries p as two FP16 operands, the
+ * high part hi = RNE_fp16(p) and the residual res = RNE_fp16(p - hi), both
+ * multiplied with the same FP16 V operand ("[Kernel][SM70] Add opt-in E4M3
+ * grouped attention with FP32 partials", historical scope list: the PV
+ * probability as high/residual FP16 operands); the row sums take hi + res
+ * the same way. The kernel evaluates p as 2^(s - m_ref + 7), so the largest
+ * p of a row is at least 2^7 and res stays an FP16 normal number for every
+ * key within 2^-10 of it: no scaling of res (nor of V) is needed, and p
+ * reaches PV with about 22 significant bits instead of 11. Any KV format.
+ * PFS_PV_FP16 (1, opt-in) carries p as hi alone: about half the PV matrix
+ * work, but the FP16 rounding of each probability (2^-11 relative) reaches
+ * the output; with attention concentrated on a few keys whose V values
+ * nearly cancel it can exceed an absolute error of 4e-3. */
+enum { PFS_PV_HIGH_RESIDUAL = 0, PFS_PV_FP16 = 1 };
 
 /* Opaque HIP stream handle (hipStream_t); NULL is the default stream. */
 typedef struct ihipStream_t* pfs_stream_t;
@@ -115,14 +121,17 @@ typedef struct pfs_problem {
     int32_t tokens_per_split;   /* 0 = library default: a function of the shape only, the
                                    smallest multiple of 64 (at least 256, at most the
                                    capacity rounded up to 64) for which one round of
-                                   split workgroups fills the GPU, capped for
+                                   split workgroups fills num_cus compute units, capped for
                                    batch > 1 at 2^20 / (2 * head_dim) tokens (about 1 MiB
                                    of K+V per request and KV head) so that requests of
                                    unequal live length can be balanced; else a multiple
                                    of partition_tokens, at most 16384 */
     int32_t kv_format;          /* PFS_KV_E4M3 (0) or PFS_KV_E5M2 (1): how the pool bytes decode */
-    int32_t pv_residual;        /* 0: P enters PV as one FP16 operand; 1: as an FP16 high part
-                                   plus an FP16 residual (see below); E4M3 only */
+    int32_t pv_mode;            /* PFS_PV_HIGH_RESIDUAL (0, default) or PFS_PV_FP16 (1), see above */
+    int32_t num_cus;            /* compute units the default split length fills (the device's
+                                   count, e.g. hipDeviceProp_t.multiProcessorCount); 0 = 256,
+                                   the MI355X's. Used only when tokens_per_split == 0; a plan
+                                   made for one count runs correctly on any device */
     int64_t kv_page_stride;     /* bytes, multiple of 16 */
     int64_t kv_token_stride;    /* bytes, multiple of 16 */
     int64_t kv_head_stride;     /* bytes, multiple of 16, >= head_dim */
@@ -132,10 +141,16 @@ typedef struct pfs_problem {
 
 typedef struct pfs_plan pfs_plan;
 
-/* The PFS_ABI_VERSION the library was built with. */
+/* The PFS_ABI_VERSION the library was built with ("[Bugfix] Use FP32 state
+ * and E4M3 defaults for DFlash2", Purpose: a stale native library is
+ * rejected, not silently used). */
 int32_t pfs_abi_version(void);
 
-/* Static, NUL-terminated description of a status code. Never NULL. */
+/* Static, NUL-terminated description of a status code; never NULL, and
+ * "unknown status" for a value that is not a PFS_* code. Every failure is
+ * reported through these codes, none is handled by a fallback
+ * ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+ * historical scope list: unsupported shapes and stale libraries fail closed). */
 const char* pfs_status_string(int32_t status);
 
 /*
@@ -152,9 +167,20 @@ const char* pfs_status_string(int32_t status);
  */
 int32_t pfs_plan_create(const pfs_problem* problem, pfs_plan** out);
 
+/* Releases a plan made by pfs_plan_create (host memory only; NULL is a
+ * no-op). The caller must not use the plan afterwards, nor destroy it while
+ * another host thread is enqueuing work with it; work already enqueued does
+ * not reference the plan. */
 void pfs_plan_destroy(pfs_plan* plan);
 
-/* Bytes of device workspace pfs_verify needs for this plan (> 0). */
+/* Bytes of device workspace pfs_verify needs for this plan (> 0; 0 for a
+ * NULL plan): the FP32 (max, sum) pairs followed by the FP32 unnormalized
+ * accumulators of every (split, request, KV head, row), each array 256-byte
+ * aligned. The workspace is owned by the caller and typed by the plan's FP32
+ * partials ("[Bugfix] Use FP32 state and E4M3 defaults for DFlash2", Test
+ * Plan and Results: workspaces kept separate per dtype; "[Kernel][SM70] Add
+ * opt-in E4M3 grouped attention with FP32 partials", final status: the
+ * workspace grows from [80,8,6] LSE values to [80,8,6,2] max/sum pairs). */
 int64_t pfs_plan_workspace_bytes(const pfs_plan* plan);
 
 /* Splits per request and tokens per split chosen by the plan. */
@@ -162,7 +188,12 @@ int32_t pfs_plan_num_splits(const pfs_plan* plan);
 int32_t pfs_plan_tokens_per_split(const pfs_plan* plan);
 
 /*
- * Enqueue one verify-attention step on `stream`.
+ * Enqueue one verify-attention step on `stream`: the operation stated at the
+ * top of this file ("[Kernel][SM70] Add opt-in E4M3 grouped attention with
+ * FP32 partials", final status and historical scope list: dense small-query
+ * verify over E4M3 KV with per-query device lengths; "[Bugfix] Use FP32 state
+ * and E4M3 defaults for DFlash2", Purpose: FP32 partial state, FP16
+ * operands and outputs, FP8 KV storage).
  *   q_fp16       device [batch, q, num_q_heads, head_dim] FP16, 16-byte aligned
  *   k_pool/v_pool device byte pools (layout above), 16-byte aligned
  *   k_scale/v_scale device [num_kv_heads] FP32 (read on device)
@@ -193,10 +224,19 @@ int32_t pfs_verify(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_po
  * The two phases of pfs_verify, for callers that time or schedule them apart.
  * pfs_verify_split runs the split kernel (dequant-on-load, QK^T, online
  * softmax, PV) and leaves every split's FP32 (max, sum, unnormalized PV) in
- * the workspace; pfs_verify_combine reads those partials, rescales them, sums
- * them in ascending split order, normalizes and writes the FP16 output.
- * pfs_verify_split followed by pfs_verify_combine on the same stream, plan and
- * workspace is exactly pfs_verify. Arguments and errors as for pfs_verify.
+ * the workspace; pfs_verify_combine reads those partials, rescales them,
+ * sums them, normalizes and writes the FP16 output. The order of the sum is
+ * fixed by the plan alone (never by timing or device data), so repeated
+ * calls give bit-identical outputs:
+ *   - plans with at most 32 splits: splits 0, 1, 2, ... one after another;
+ *   - more splits: the S splits are cut into 8 contiguous blocks of
+ *     ceil(S / 8); each block is summed in ascending split order, then the
+ *     8 block sums are combined in a fixed pairwise tree, (0+1), (2+3),
+ *     (4+5), (6+7), then (01+23), (45+67), then (0123+4567).
+ * Before each addition the two operands are rescaled to their common
+ * maximum. pfs_verify_split followed by pfs_verify_combine on the same
+ * stream, plan and workspace is exactly pfs_verify. Arguments and errors as
+ * for pfs_verify.
  */
 int32_t pfs_verify_split(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool,
                          const uint8_t* v_pool, const float* k_scale, const int32_t* block_table,
@@ -207,9 +247,10 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
                            pfs_stream_t stream);
 
 /*
- * Paged FP8 -> FP16 bridge (the dequant-on-load path exposed on its own;
- * "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
- * Scope list: an explicit E4M3 paged-to-FP16 bridge API).
+ * Paged FP8 -> FP16 bridge: the dequant-on-load path as a call of its own,
+ * turning paged E4M3 (or E5M2) bytes into a dense FP16 array
+ * ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
+ * historical scope list, the bridge between the two representations).
  * Writes out_fp16 as a dense device array [batch, capacity, num_kv_heads,
  * head_dim] (capacity = max_pages_per_row * page_size): element (b, t, g, d)
  * is dec(byte) * scale[g] rounded once to the nearest FP16 (ties to even),

@@ -12,7 +12,8 @@ from __future__ import annotations
 import math
 from typing import Dict, Optional, Sequence, Tuple
 
-__all__ = ["verify", "dequant_paged", "kv_append", "make_plan", "Plan", "PfsError", "ABI_VERSION", "KV_FORMATS"]
+__all__ = ["verify", "dequant_paged", "kv_append", "make_plan", "Plan", "PfsError", "ABI_VERSION", "KV_FORMATS",
+           "PV_MODES"]
 
 _plans: Dict[Tuple, "Plan"] = {}
 
@@ -26,6 +27,24 @@ def __getattr__(name):
 
 
 KV_FORMATS = {"e4m3": 0, "e5m2": 1}
+# how each probability enters the PV product (include/pfs.h, PFS_PV_*)
+PV_MODES = {"high_residual": 0, "fp16": 1}
+
+
+def _pv_mode(pv_mode: str) -> int:
+    if pv_mode not in PV_MODES:
+        raise ValueError(f"pv_mode must be one of {sorted(PV_MODES)}, got {pv_mode!r}")
+    return PV_MODES[pv_mode]
+
+
+def _num_cus(t) -> int:
+    """Compute units of the device holding tensor t (0, the library default,
+    for a host tensor)."""
+    import torch
+
+    if not t.is_cuda:
+        return 0
+    return int(torch.cuda.get_device_properties(t.device).multi_processor_count)
 
 
 def _kv_format(pool, kv_format: Optional[str]) -> int:
@@ -54,8 +73,10 @@ def _pool_layout(pool):
 
 def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_scale=None,
               partition_tokens=64, tokens_per_split=0, kv_format: Optional[str] = None,
-              pv_residual: bool = False):
-    """Plan (cached) for a problem whose KV pools look like ``k_pool``."""
+              pv_mode: str = "high_residual", num_cus: Optional[int] = None):
+    """Plan (cached) for a problem whose KV pools look like ``k_pool``; the
+    default split length fills the compute units of ``k_pool``'s device
+    unless ``num_cus`` is given."""
     from . import _lib
 
     pages, page, hkv, d, (sp, st, sh) = _pool_layout(k_pool)
@@ -63,22 +84,25 @@ def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     hm = tuple(int(x) for x in head_map)
+    pm = _pv_mode(pv_mode)
+    cus = _num_cus(k_pool) if num_cus is None else int(num_cus)
     key = (batch, q, num_q_heads, hkv, d, page, max_pages_per_row, pages, sp, st, sh, float(sm_scale), hm,
-           partition_tokens, tokens_per_split, fmt, bool(pv_residual))
+           partition_tokens, tokens_per_split, fmt, pm, cus)
     plan = _plans.get(key)
     if plan is None:
         plan = _lib.Plan(batch=batch, q=q, num_q_heads=num_q_heads, num_kv_heads=hkv, head_dim=d, page_size=page,
                          max_pages_per_row=max_pages_per_row, num_pool_pages=pages, kv_page_stride=sp,
                          kv_token_stride=st, kv_head_stride=sh, sm_scale=sm_scale, head_map=hm,
                          partition_tokens=partition_tokens, tokens_per_split=tokens_per_split, kv_format=fmt,
-                         pv_residual=int(bool(pv_residual)))
+                         pv_mode=pm, num_cus=cus)
         _plans[key] = plan
     return plan
 
 
 def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_map: Optional[Sequence[int]] = None,
            sm_scale: Optional[float] = None, partition_tokens: int = 64, tokens_per_split: int = 0, out=None,
-           workspace=None, stream=None, plan=None, kv_format: Optional[str] = None, pv_residual: bool = False):
+           workspace=None, stream=None, plan=None, kv_format: Optional[str] = None,
+           pv_mode: str = "high_residual"):
     """Verify attention of q draft rows per request over a paged FP8 KV cache.
 
     q            [B, q, Hq, D] float16, contiguous, on the GPU
@@ -87,8 +111,10 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
                  16 bytes)
     kv_format    "e4m3" (default) or "e5m2"; a float8_e4m3fn / float8_e5m2
                  pool dtype implies it
-    pv_residual  carry each probability into PV as an FP16 high part plus an
-                 FP16 residual scaled by 2048 (E4M3 only; twice the PV work)
+    pv_mode      "high_residual" (default): each probability enters PV as an
+                 FP16 high part plus an FP16 residual (about 22 bits);
+                 "fp16": as one FP16 operand (about half the PV matrix work,
+                 2^-11 relative rounding per probability)
     k_scale/v_scale [Hkv] float32
     block_table  [B, max_pages_per_row] int32
     live_len     [B] int32, draft tokens included
@@ -110,7 +136,7 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
         plan = make_plan(batch=B, q=nq, num_q_heads=Hq, head_map=head_map, k_pool=k_pool,
                          max_pages_per_row=int(block_table.shape[1]), sm_scale=sm_scale,
                          partition_tokens=partition_tokens, tokens_per_split=tokens_per_split,
-                         kv_format=kv_format, pv_residual=pv_residual)
+                         kv_format=kv_format, pv_mode=pv_mode)
     elif plan.kv_format != _kv_format(k_pool, kv_format):
         raise ValueError("the plan's KV format differs from the pools'")
     if v_pool.dtype != k_pool.dtype:

@@ -61,7 +61,8 @@ class PfsProblem(ctypes.Structure):
         ("partition_tokens", ctypes.c_int32),
         ("tokens_per_split", ctypes.c_int32),
         ("kv_format", ctypes.c_int32),
-        ("pv_residual", ctypes.c_int32),
+        ("pv_mode", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
         ("kv_page_stride", ctypes.c_int64),
         ("kv_token_stride", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64),
@@ -130,14 +131,14 @@ class Plan:
 
     def __init__(self, *, batch, q, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_row,
                  num_pool_pages, kv_page_stride, kv_token_stride, kv_head_stride, sm_scale, head_map,
-                 partition_tokens=64, tokens_per_split=0, kv_format=0, pv_residual=0):
+                 partition_tokens=64, tokens_per_split=0, kv_format=0, pv_mode=0, num_cus=0):
         lib = load()
         self._lib = lib
         self._handle = None
         hm = (ctypes.c_int32 * int(num_q_heads))(*[int(x) for x in head_map])
         self.problem = PfsProblem(int(batch), int(q), int(num_q_heads), int(num_kv_heads), int(head_dim),
                                   int(page_size), int(max_pages_per_row), int(num_pool_pages),
-                                  int(partition_tokens), int(tokens_per_split), int(kv_format), int(pv_residual),
+                                  int(partition_tokens), int(tokens_per_split), int(kv_format), int(pv_mode), int(num_cus),
                                   int(kv_page_stride),
                                   int(kv_token_stride), int(kv_head_stride), float(sm_scale),
                                   ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32)))
@@ -151,7 +152,8 @@ class Plan:
         self.tokens_per_split = int(lib.pfs_plan_tokens_per_split(handle))
         self.capacity = int(max_pages_per_row) * int(page_size)
         self.kv_format = int(kv_format)
-        self.pv_residual = int(pv_residual)
+        self.pv_mode = int(pv_mode)
+        self.num_cus = int(num_cus)
 
     @property
     def handle(self):

@@ -18,7 +18,7 @@ constexpr int max_row_tiles(int head_dim) { return head_dim >= 256 ? 1 : (head_d
 // Byte offsets of the 16-token tiles of one split sit in an LDS table.
 constexpr int kTileTableEntries = 1024;
 constexpr int kMaxTokensPerSplit = 16 * kTileTableEntries;
-constexpr int kCUs = 256;  // MI355X compute units
+constexpr int kDefaultCUs = 256;  // MI355X compute units: the default split length fills them
 
 // A split workgroup has W = RG * TP waves: RG row groups (RT row tiles each)
 // times TP token lanes; a stage holds TP 32-token steps of K and V bytes.

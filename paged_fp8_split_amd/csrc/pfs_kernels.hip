@@ -50,15 +50,25 @@
 //
 // Numerics: FP16 MFMA operands with FP32 accumulation; the per-head K scale,
 // the softmax scale and log2(e) are applied to FP32 scores (inside the exp2
-// argument); probabilities are exp2(s - m_ref + 7) rounded once to FP16
-// against a lazily raised reference maximum m_ref; the row sums come from the
-// matrix core (a ones row times the same FP16 P the PV product uses); V's
-// scale is applied once in the combine. Masked scores are selected to -inf and
-// K/V bytes beyond the live length are never loaded (zero), so NaN (or E5M2
-// infinity) tail bytes cannot leak. With RES (high/residual probabilities,
-// "[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",
-// historical scope) each P is also carried as an FP16 residual scaled by
-// 2^11, multiplied with V and folded in times 2^-11, so P reaches ~22 bits.
+// argument); probabilities are p = exp2(s - m_ref + 7) against a lazily
+// raised reference maximum m_ref; the row sums come from the matrix core (a
+// ones row times the same FP16 operands the PV product uses); V's scale is
+// applied once in the combine. Masked scores are selected to -inf and K/V
+// bytes beyond the live length are never loaded (zero), so NaN (or E5M2
+// infinity) tail bytes cannot leak.
+//
+// Probabilities (RES, the default; "[Kernel][SM70] Add opt-in E4M3 grouped
+// attention with FP32 partials", historical scope: high/residual FP16 PV
+// operands): each p enters PV as hi = RNE_fp16(p) plus res = RNE_fp16(p - hi),
+// both multiplied with the same FP16 V operand into the same accumulators.
+// p - hi is exact in FP32. Because p carries the factor 2^7, the maximum of a
+// row has p >= 2^7, and res is an FP16 normal number for every key down to
+// 2^-10 of that maximum, so hi + res carries p to about 22 bits with no
+// scaling of the residual or of V. (On the pages p <= 1, so their residual
+// needs a 2^11 scale to stay out of FP16 subnormals, and V a matching inverse
+// scale.) Keys further down lose at most 2^-25 absolute, 2^-32 of the row's
+// sum. Without RES (opt-in) p enters as hi only: FP16's 2^-11 relative
+// rounding of each probability then reaches the output.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -112,18 +122,22 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
     return bit_cast_<f16x8>(r);
 }
 
-// 8 E4M3 bytes -> 8 FP16 values times 2^-11, exact: the smallest E4M3
-// magnitude, 2^-9, becomes 2^-20, a multiple of FP16's 2^-24 subnormal step,
-// and every E4M3 significand (4 bits) fits. The operand of the residual
-// probabilities (which carry a factor 2^11).
-__device__ __forceinline__ f16x8 e4m3x8_to_f16x8_res(uint32_t w0, uint32_t w1) {
-    constexpr float kInv = 1.0f / 2048.0f;
-    u32x4 r;
-    r.x = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, kInv, false));
-    r.y = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, kInv, true));
-    r.z = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, kInv, false));
-    r.w = bit_cast_<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, kInv, true));
-    return bit_cast_<f16x8>(r);
+// Residuals of a pair of probabilities: given hi = (RNE_fp16(p0),
+// RNE_fp16(p1)) packed, returns (RNE_fp16(p0 - hi.x), RNE_fp16(p1 - hi.y))
+// packed. v_fma_mix{lo,hi}_f16 reads the FP16 half of hi as an FP32 operand,
+// forms p * 1 - hi in one fused step (exact: p - hi is an FP32 number) and
+// rounds once to FP16 into the low or high half of the result: two
+// instructions where the plain sequence (convert back, subtract, convert)
+// takes six. Register operands only; the low half is written first, and
+// the early-clobber output keeps it apart from the inputs the second
+// instruction still reads.
+__device__ __forceinline__ uint32_t residual_f16x2(float p0, float p1, uint32_t hi) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "=&v"(r)
+        : "v"(p0), "v"(p1), "v"(hi));
+    return r;
 }
 
 // Max over the four lanes l, l^16, l^32, l^48 (the lane groups holding one
@@ -440,22 +454,13 @@ pfs_split_kernel(const SplitArgs a) {
     float cscale = a.sm_scale_log2e * kscale_g;  // score scale, log2 domain
 
     f32x4 acc[MD][RT];
-    f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 P
-    // with RES at head_dim 256: the residual products go to accumulators of
-    // their own (against the unscaled V operand) and are folded in times
-    // 2^-11 after the last step
-    constexpr bool RES_ACC = RES && D == 256;
-    f32x4 acc_res[RES_ACC ? MD : 1][RT];
-    f32x4 lacc_res[RT];
+    f32x4 lacc[RT];  // row sums, computed by the matrix core from the same FP16 operands
     float mref[RT], nb[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) {
         mref[nt] = -INFINITY;
         nb[nt] = 0.0f;
         lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lacc_res[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int md = 0; md < (RES_ACC ? MD : 1); ++md) acc_res[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int md = 0; md < MD; ++md) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -463,7 +468,6 @@ pfs_split_kernel(const SplitArgs a) {
     const _Float16 one_or_zero = (lc == 0) ? (_Float16)1.0f : (_Float16)0.0f;
     const f16x8 ones = f16x8{one_or_zero, one_or_zero, one_or_zero, one_or_zero,
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
-    const f16x8 ones_res = ones * (_Float16)(1.0f / 2048.0f);  // row 0 = 2^-11, for the residual sums
 
     // transposed V reads: lane j of each 16-lane block names 8 bytes of token
     // tok(lg, j >> 1) of the step, the (j & 1) half of a 16-byte chunk. With
@@ -613,9 +617,9 @@ pfs_split_kernel(const SplitArgs a) {
     };
     // online softmax, log2 domain, lazy reference maximum. Scores are scaled
     // before masking, so a masked score is exactly -inf for any finite K scale.
-    // The FP16 probabilities of one step: hi = RNE_fp16(P) and, when RES, the
-    // residual res = RNE_fp16((P - hi) * 2^11), so that hi + res * 2^-11
-    // carries P to about 22 bits.
+    // The FP16 operands of one step's probabilities: hi = RNE_fp16(p) and,
+    // with RES, res = RNE_fp16(p - hi), so that hi + res carries p to about
+    // 22 bits.
     struct Probs {
         f16x8 hi[RT];
         f16x8 res[RT];
@@ -654,11 +658,6 @@ pfs_split_kernel(const SplitArgs a) {
                     lacc[nt] *= al;
 #pragma unroll
                     for (int md = 0; md < MD; ++md) acc[md][nt] *= al;
-                    if constexpr (RES_ACC) {
-                        lacc_res[nt] *= al;
-#pragma unroll
-                        for (int md = 0; md < MD; ++md) acc_res[md][nt] *= al;
-                    }
                     mref[nt] = m_new;
                     nb[nt] = kPBias - m_new;
                 }
@@ -668,23 +667,17 @@ pfs_split_kernel(const SplitArgs a) {
         // finite: it only changes together with a finite m_ref)
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            f16x2 pp[4], pr_res[4];
+            uint32_t hw[4], rw[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float c = edge ? 1.0f : cscale;
                 const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e], c, nb[nt]));
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[nt][e + 1], c, nb[nt]));
-                const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-                pp[e >> 1] = f16x2{h0, h1};
-                if constexpr (RES)  // p - hi is exact in FP32, and so is the scaling by 2^11
-                    pr_res[e >> 1] = f16x2{(_Float16)((p0 - (float)h0) * 2048.0f),
-                                           (_Float16)((p1 - (float)h1) * 2048.0f)};
+                hw[e >> 1] = bit_cast_<uint32_t>(f16x2{(_Float16)p0, (_Float16)p1});
+                if constexpr (RES) rw[e >> 1] = residual_f16x2(p0, p1, hw[e >> 1]);
             }
-            pr.hi[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pp[0]), bit_cast_<uint32_t>(pp[1]),
-                                               bit_cast_<uint32_t>(pp[2]), bit_cast_<uint32_t>(pp[3])});
-            if constexpr (RES)
-                pr.res[nt] = bit_cast_<f16x8>(u32x4{bit_cast_<uint32_t>(pr_res[0]), bit_cast_<uint32_t>(pr_res[1]),
-                                                    bit_cast_<uint32_t>(pr_res[2]), bit_cast_<uint32_t>(pr_res[3])});
+            pr.hi[nt] = bit_cast_<f16x8>(u32x4{hw[0], hw[1], hw[2], hw[3]});
+            if constexpr (RES) pr.res[nt] = bit_cast_<f16x8>(u32x4{rw[0], rw[1], rw[2], rw[3]});
         }
     };
     // O^T += V^T * P^T for head_dim tiles [md0, md0 + 4), V^T read transposed from LDS
@@ -700,40 +693,35 @@ pfs_split_kernel(const SplitArgs a) {
         }
         return vc;
     };
-    // (with RES, also O^T += (V^T * 2^-11) * RES^T into the same accumulators)
+    // (with RES, also O^T += V^T * RES^T, against the same V operand and into
+    // the same accumulators, after the high parts of the chunk)
     auto pv_fold = [&](const VChunk& vc, int md0, const Probs& pr) __attribute__((always_inline)) {
+        f16x8 vop[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f16x8 vop = fp8x8_to_f16x8<FMT>((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
+            vop[u] = fp8x8_to_f16x8<FMT>((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt)
-                acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pr.hi[nt], acc[md0 + u][nt], 0, 0, 0);
-            if constexpr (RES_ACC) {
+                acc[md0 + u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[u], pr.hi[nt], acc[md0 + u][nt], 0, 0, 0);
+        }
+        if constexpr (RES) {
 #pragma unroll
-                for (int nt = 0; nt < RT; ++nt)
-                    acc_res[md0 + u][nt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pr.res[nt], acc_res[md0 + u][nt], 0, 0, 0);
-            } else if constexpr (RES) {
-                const f16x8 vres = e4m3x8_to_f16x8_res((uint32_t)vc.w[u].x, (uint32_t)vc.w[u].y);
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int nt = 0; nt < RT; ++nt)
                     acc[md0 + u][nt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vres, pr.res[nt], acc[md0 + u][nt], 0, 0, 0);
-            }
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[u], pr.res[nt], acc[md0 + u][nt], 0, 0, 0);
         }
     };
     auto pv_chunk = [&](const uint8_t* sbase, int md0, const Probs& pr) __attribute__((always_inline)) {
         pv_fold(v_read(sbase, md0), md0, pr);
     };
-    // l += 1 * P^T (row sums from the same FP16 P; with RES, + 2^-11 * RES^T)
+    // l += 1 * P^T (row sums from the same FP16 operands; with RES, + 1 * RES^T)
     auto row_sums = [&](const Probs& pr) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
             lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.hi[nt], lacc[nt], 0, 0, 0);
-            if constexpr (RES_ACC)
-                lacc_res[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.res[nt], lacc_res[nt], 0, 0, 0);
-            else if constexpr (RES)
-                lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_res, pr.res[nt], lacc[nt], 0, 0, 0);
+            if constexpr (RES) lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pr.res[nt], lacc[nt], 0, 0, 0);
         }
     };
 
@@ -846,14 +834,6 @@ pfs_split_kernel(const SplitArgs a) {
         }
     }
     wait_vm_and_barrier<0>();  // no load into LDS is still in flight
-    if constexpr (RES_ACC) {  // fold the residual products in (times 2^-11, exact in FP32)
-#pragma unroll
-        for (int nt = 0; nt < RT; ++nt) {
-            lacc[nt] += lacc_res[nt] * (1.0f / 2048.0f);
-#pragma unroll
-            for (int md = 0; md < MD; ++md) acc[md][nt] += acc_res[md][nt] * (1.0f / 2048.0f);
-        }
-    }
 
     // ---- merge the TP token lanes of each row group: ((tl0 + tl2) + (tl1 + tl3)) ... ----
     const int64_t slot_base = (((int64_t)split * a.batch + b) * a.num_kv_heads + g) * a.rows;
@@ -951,120 +931,164 @@ struct CombineArgs {
     int32_t rows;
     int32_t capacity;
     int32_t tokens_per_split;
+    int32_t num_splits;
+    int32_t head_dim;
     uint8_t qhead[pfs::kMaxQHeads];
 };
 
-// Many splits: one workgroup of 256 threads per (request, KV head, row,
-// column slice), so that even one request's few rows spread over every CU.
-// With SL split lanes a workgroup covers 1024 / SL columns: thread t owns the
-// 4 columns 4 (t % (256 / SL)) .. of the slice and the visible splits s with
-// s % SL == t / (256 / SL) (its split lane), folded in ascending order CH at a
-// time (their loads are issued together) against a running maximum; the SL
-// split lanes of each column group are then merged in lane order against the
-// global maximum. Plans with at most 4 CH splits use pfs_combine_rows_kernel.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineChunk = 8;
-constexpr int kCombineRowSplits = 4 * kCombineChunk;  // the row kernel up to four rounds of loads
+// The running state of a fold over splits: reference maximum M (log2 domain),
+// weighted sum lw and weighted accumulators acc of 4 columns.
+struct FoldState {
+    float M, lw;
+    f32x4 acc;
+};
 
-template <int D, int SL>
-__global__ __launch_bounds__(kCombineThreads) void pfs_combine_kernel(const CombineArgs a) {
-    constexpr int CH = kCombineChunk;
-    constexpr int CG = kCombineThreads / SL;  // 4-column groups per workgroup
-    constexpr int SLICES = D / (4 * CG);
-    static_assert(SLICES >= 1 && D % (4 * CG) == 0, "combine slice");
-    __shared__ float part_m[SL][CG];
-    __shared__ float part_l[SL][CG];
-    __shared__ f32x4 part_acc[SL][CG];
+// Folds N splits (their (max, sum) pairs v and accumulators x, in ascending
+// split order; invalid ones selected out beforehand as (-inf, 0) and zeros)
+// into st: the maximum is raised first, the running state rescaled once, then
+// the splits are added in order.
+template <int N>
+__device__ __forceinline__ void fold_splits(FoldState& st, const float2 (&v)[N], const f32x4 (&x)[N]) {
+    float cm = st.M;
+#pragma unroll
+    for (int u = 0; u < N; ++u) cm = fmaxf(cm, v[u].x);
+    if (cm != st.M) {  // a larger maximum: rescale the running state (empty state: factor 0)
+        const float al = (st.M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.M - cm);
+        st.lw *= al;
+        st.acc *= al;
+        st.M = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const float f = (v[u].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[u].x - st.M);
+        st.lw += f * v[u].y;
+        st.acc += f * x[u];
+    }
+}
 
-    const int t = threadIdx.x;
-    const int cg = t % CG;  // column group of the slice
-    const int sl = t / CG;  // split lane
+// Loads the partials of N consecutive splits s0, s0 + 1, ... of one row
+// (slot0 + s * stride), at indices clamped to the plan's last split so that
+// no load sits under a branch; the caller selects the valid ones.
+template <int N>
+__device__ __forceinline__ void load_splits(const CombineArgs& a, int64_t slot0, int64_t stride, int s0, int col0,
+                                            float2 (&v)[N], f32x4 (&x)[N]) {
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const int64_t slot = slot0 + (int64_t)min(s0 + u, a.num_splits - 1) * stride;
+        v[u] = ml[slot];
+        x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * a.head_dim + col0);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void select_splits(int s0, int s_lim, float2 (&v)[N], f32x4 (&x)[N]) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const bool ok = s0 + u < s_lim;
+        v[u] = ok ? v[u] : make_float2(-INFINITY, 0.0f);
+        x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Many splits: one workgroup of NW waves per (request, KV head, row, column
+// slice); each wave owns 32 columns of the row. Lane (sl, cg) = (lane / 8,
+// lane % 8) owns columns 4 cg .. 4 cg + 3 of its wave's 32 and split block sl.
+// The plan's splits are cut into 8 contiguous blocks of C = ceil(S / 8)
+// splits; lane sl folds the visible splits of block sl in ascending order,
+// kCombineRound at a time with their loads issued together (the first round
+// before the live length has arrived: slots past the visible splits are read
+// and selected out). The 8 block states are then merged across the wave's
+// lanes (cross-lane permutes, no LDS) in a fixed pairwise tree: blocks (0,1),
+// (2,3), (4,5), (6,7), then (01,23), (45,67), then (0123,4567), the lower
+// blocks always the left operand. One IEEE division, one RNE to FP16.
+constexpr int kCombineSplitLanes = 8;
+constexpr int kCombineRound = 16;
+constexpr int kCombineRowSplits = 32;  // at most this many splits: pfs_combine_rows_kernel
+
+__device__ __forceinline__ float lane_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <int D>
+__global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
+    constexpr int SL = kCombineSplitLanes;
+    constexpr int CGW = 64 / SL;                    // 4-column groups per wave (32 columns)
+    constexpr int NW = D / 32 < 4 ? D / 32 : 4;     // waves per workgroup
+    constexpr int COLS = 32 * NW;                   // columns per workgroup
+    constexpr int SLICES = D / COLS;
+    constexpr int R = kCombineRound;
+    static_assert(SLICES * COLS == D, "combine slice");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sl = lane / CGW;
+    const int cg = lane % CGW;
     const int r = blockIdx.x / SLICES;
-    const int col0 = (blockIdx.x % SLICES) * (4 * CG) + 4 * cg;
+    const int col0 = (blockIdx.x % SLICES) * COLS + 32 * wave + 4 * cg;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
     const int i = r / a.group;
     const int h = a.qhead[g * a.group + (r % a.group)];
     _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + col0;
+    const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;  // between splits
+    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
+    const int C = (a.num_splits + SL - 1) / SL;
+    const int s_begin = sl * C;
+    const int s_end = min(s_begin + C, a.num_splits);
 
-    const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
+    const int32_t L_raw = a.live_len[b];
+    float2 v[R];
+    f32x4 x[R];
+    load_splits<R>(a, slot0, stride, s_begin, col0, v, x);
+    const int32_t L = clamp_i(L_raw, 0, a.capacity);
     const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
-    if (n == 0) {  // nothing visible: defined output +0.0
-        if (sl == 0) {
+    const int ns = (n + a.tokens_per_split - 1) / a.tokens_per_split;  // splits holding visible keys
+    const int s_lim = min(s_end, ns);
+    FoldState st{-INFINITY, 0.0f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    select_splits<R>(s_begin, s_lim, v, x);
+    fold_splits<R>(st, v, x);
+    for (int s0 = s_begin + R; s0 < s_lim; s0 += R) {
+        load_splits<R>(a, slot0, stride, s0, col0, v, x);
+        select_splits<R>(s0, s_lim, v, x);
+        fold_splits<R>(st, v, x);
+    }
+    // pairwise tree over the 8 blocks (lane bits 3, 4, 5 select the block)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dst[c] = (_Float16)0.0f;
-        }
+    for (int bit = CGW; bit < 64; bit <<= 1) {
+        const float oM = lane_xor(st.M, bit);
+        const float ol = lane_xor(st.lw, bit);
+        f32x4 oa;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) oa[c] = lane_xor(st.acc[c], bit);
+        const bool upper = (lane & bit) != 0;  // this lane holds the right operand
+        const float Ml = upper ? oM : st.M, Mr = upper ? st.M : oM;
+        const float ll = upper ? ol : st.lw, lr = upper ? st.lw : ol;
+        const f32x4 al = upper ? oa : st.acc, ar = upper ? st.acc : oa;
+        const float Mg = fmaxf(Ml, Mr);
+        const float fl = (Ml == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Ml - Mg);
+        const float fr = (Mr == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Mr - Mg);
+        st.M = Mg;
+        st.lw = fl * ll + fr * lr;
+        st.acc = fl * al + fr * ar;
+    }
+    if (sl != 0) return;
+    if (n == 0) {  // nothing visible: defined output +0.0
+        *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
         return;
     }
-    const int ns = (n + a.tokens_per_split - 1) / a.tokens_per_split;  // splits holding visible keys
-    const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;   // between splits
-    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
-    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
-
-    float M = -INFINITY, lw = 0.0f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = sl; c0 < ns; c0 += SL * CH) {
-        float2 v[CH];
-        f32x4 x[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int sp = c0 + u * SL;
-            if (sp < ns) {
-                const int64_t slot = slot0 + sp * stride;
-                v[u] = ml[slot];
-                x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + col0);
-            } else {
-                v[u] = make_float2(-INFINITY, 0.0f);
-                x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        float cm = M;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) cm = fmaxf(cm, v[u].x);
-        if (cm != M) {  // a larger maximum: rescale the running state (empty state: factor 0)
-            const float al = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
-            lw *= al;
-            acc *= al;
-            M = cm;
-        }
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const float f = (v[u].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[u].x - M);
-            lw += f * v[u].y;
-            acc += f * x[u];
-        }
-    }
-    part_m[sl][cg] = M;
-    part_l[sl][cg] = lw;
-    part_acc[sl][cg] = acc;
-    __syncthreads();
-    if (sl != 0) return;
-    float Mg = part_m[0][cg];
-#pragma unroll
-    for (int k = 1; k < SL; ++k) Mg = fmaxf(Mg, part_m[k][cg]);
-    float lt = 0.0f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < SL; ++k) {
-        const float fw = (part_m[k][cg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(part_m[k][cg] - Mg);
-        lt += fw * part_l[k][cg];
-        num += fw * part_acc[k][cg];
-    }
     const float vs = a.vscale[g];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((num[c] * vs) / lt);
+    f16x2 o01 = f16x2{(_Float16)((st.acc[0] * vs) / st.lw), (_Float16)((st.acc[1] * vs) / st.lw)};
+    f16x2 o23 = f16x2{(_Float16)((st.acc[2] * vs) / st.lw), (_Float16)((st.acc[3] * vs) / st.lw)};
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bit_cast_<uint32_t>(o01), bit_cast_<uint32_t>(o23));
 }
 
-
-// Few splits (at most 4 CH): one thread per 4 columns of one row folds every
-// visible split of that row itself (in ascending order, CH loads issued
-// together, running maximum) with no cross-lane merge; a workgroup covers
-// 1024 / D whole rows.
+// Few splits (at most kCombineRowSplits): one thread per 4 columns of one row
+// folds every visible split of that row itself, in ascending order, 8 at a
+// time (the first 8 loads issued before the live length has arrived), with
+// no cross-lane merge; a workgroup covers 1024 / D whole rows.
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void pfs_combine_rows_kernel(const CombineArgs a) {
-    constexpr int CH = kCombineChunk;
-    constexpr int TPR = D / 4;                   // threads per row
-    constexpr int RPW = kCombineThreads / TPR;   // rows per workgroup
+__global__ __launch_bounds__(256) void pfs_combine_rows_kernel(const CombineArgs a) {
+    constexpr int R = 8;
+    constexpr int TPR = D / 4;        // threads per row
+    constexpr int RPW = 256 / TPR;    // rows per workgroup
     const int t = threadIdx.x;
     const int r = blockIdx.x * RPW + t / TPR;
     if (r >= a.rows) return;
@@ -1074,53 +1098,32 @@ __global__ __launch_bounds__(kCombineThreads) void pfs_combine_rows_kernel(const
     const int i = r / a.group;
     const int h = a.qhead[g * a.group + (r % a.group)];
     _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + col0;
-    const int32_t L = clamp_i(a.live_len[b], 0, a.capacity);
-    const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
-    if (n == 0) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[c] = (_Float16)0.0f;
-        return;
-    }
-    const int ns = (n + a.tokens_per_split - 1) / a.tokens_per_split;
     const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
-    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
-    float M = -INFINITY, lw = 0.0f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < ns; c0 += CH) {
-        float2 v[CH];
-        f32x4 x[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int sp = c0 + u;
-            if (sp < ns) {
-                const int64_t slot = slot0 + sp * stride;
-                v[u] = ml[slot];
-                x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * D + col0);
-            } else {
-                v[u] = make_float2(-INFINITY, 0.0f);
-                x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        float cm = M;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) cm = fmaxf(cm, v[u].x);
-        if (cm != M) {
-            const float al = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
-            lw *= al;
-            acc *= al;
-            M = cm;
-        }
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const float f = (v[u].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[u].x - M);
-            lw += f * v[u].y;
-            acc += f * x[u];
-        }
+
+    const int32_t L_raw = a.live_len[b];
+    float2 v[R];
+    f32x4 x[R];
+    load_splits<R>(a, slot0, stride, 0, col0, v, x);
+    const int32_t L = clamp_i(L_raw, 0, a.capacity);
+    const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
+    if (n == 0) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+        return;
+    }
+    const int ns = min((n + a.tokens_per_split - 1) / a.tokens_per_split, a.num_splits);
+    FoldState st{-INFINITY, 0.0f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    select_splits<R>(0, ns, v, x);
+    fold_splits<R>(st, v, x);
+    for (int s0 = R; s0 < ns; s0 += R) {
+        load_splits<R>(a, slot0, stride, s0, col0, v, x);
+        select_splits<R>(s0, ns, v, x);
+        fold_splits<R>(st, v, x);
     }
     const float vs = a.vscale[g];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) dst[c] = (_Float16)((acc[c] * vs) / lw);
+    f16x2 o01 = f16x2{(_Float16)((st.acc[0] * vs) / st.lw), (_Float16)((st.acc[1] * vs) / st.lw)};
+    f16x2 o23 = f16x2{(_Float16)((st.acc[2] * vs) / st.lw), (_Float16)((st.acc[3] * vs) / st.lw)};
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bit_cast_<uint32_t>(o01), bit_cast_<uint32_t>(o23));
 }
 
 template <int D, int RT, int RG, int FMT, bool RES, bool NARROW = false>
@@ -1214,13 +1217,14 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256) return PFS_ERR_UNSUPPORTED;
     hipError_t e;
-    // the residual probabilities exist for E4M3 only (the plan rejects E5M2 with them)
-    if (p.kv_format == PFS_KV_E4M3 && p.pv_residual)
-        e = launch_split_fmt<PFS_KV_E4M3, true>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
-    else if (p.kv_format == PFS_KV_E4M3)
-        e = launch_split_fmt<PFS_KV_E4M3, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
-    else if (p.kv_format == PFS_KV_E5M2 && !p.pv_residual)
-        e = launch_split_fmt<PFS_KV_E5M2, false>(sa, p.head_dim, plan->row_tiles, plan->row_groups, plan->waves, s);
+    const bool res = p.pv_mode == PFS_PV_HIGH_RESIDUAL;
+    const int32_t rt = plan->row_tiles, rg = plan->row_groups, w = plan->waves;
+    if (p.kv_format == PFS_KV_E4M3)
+        e = res ? launch_split_fmt<PFS_KV_E4M3, true>(sa, p.head_dim, rt, rg, w, s)
+                : launch_split_fmt<PFS_KV_E4M3, false>(sa, p.head_dim, rt, rg, w, s);
+    else if (p.kv_format == PFS_KV_E5M2)
+        e = res ? launch_split_fmt<PFS_KV_E5M2, true>(sa, p.head_dim, rt, rg, w, s)
+                : launch_split_fmt<PFS_KV_E5M2, false>(sa, p.head_dim, rt, rg, w, s);
     else
         return PFS_ERR_UNSUPPORTED;
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
@@ -1243,29 +1247,29 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.rows = plan->rows;
     ca.capacity = plan->capacity;
     ca.tokens_per_split = plan->tokens_per_split;
+    ca.num_splits = plan->num_splits;
+    ca.head_dim = p.head_dim;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (plan->num_splits <= kCombineRowSplits) {  // each thread folds every split of its row
-        const dim3 rgrid((plan->rows * p.head_dim / 4 + kCombineThreads - 1) / kCombineThreads, p.num_kv_heads,
-                         p.batch);
+        const dim3 rgrid((plan->rows * p.head_dim / 4 + 255) / 256, p.num_kv_heads, p.batch);
         switch (p.head_dim) {
-            case 64: hipLaunchKernelGGL(pfs_combine_rows_kernel<64>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
-            case 128: hipLaunchKernelGGL(pfs_combine_rows_kernel<128>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
-            case 256: hipLaunchKernelGGL(pfs_combine_rows_kernel<256>, rgrid, dim3(kCombineThreads), 0, s, ca); break;
+            case 64: hipLaunchKernelGGL(pfs_combine_rows_kernel<64>, rgrid, dim3(256), 0, s, ca); break;
+            case 128: hipLaunchKernelGGL(pfs_combine_rows_kernel<128>, rgrid, dim3(256), 0, s, ca); break;
+            case 256: hipLaunchKernelGGL(pfs_combine_rows_kernel<256>, rgrid, dim3(256), 0, s, ca); break;
             default: return PFS_ERR_UNSUPPORTED;
         }
         return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
     }
-    // more splits: 16 split lanes per column group, 64-column slices
-    constexpr int SL = 16;
-    const dim3 grid(plan->rows * (p.head_dim * SL / 1024), p.num_kv_heads, p.batch);
-    const dim3 block(kCombineThreads);
+    // more splits: 32 columns per wave, up to four waves (128 columns) per workgroup
+    const int nw = p.head_dim / 32 < 4 ? p.head_dim / 32 : 4;
+    const dim3 grid(plan->rows * (p.head_dim / (32 * nw)), p.num_kv_heads, p.batch);
+    const dim3 block(64 * nw);
     switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL((pfs_combine_kernel<64, SL>), grid, block, 0, s, ca); break;
-        case 128: hipLaunchKernelGGL((pfs_combine_kernel<128, SL>), grid, block, 0, s, ca); break;
-        case 256: hipLaunchKernelGGL((pfs_combine_kernel<256, SL>), grid, block, 0, s, ca); break;
+        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, block, 0, s, ca); break;
+        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, block, 0, s, ca); break;
+        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, block, 0, s, ca); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
-

@@ -82,8 +82,8 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
     if (p.page_size % 16 != 0) return PFS_ERR_UNSUPPORTED;
     if (p.partition_tokens != pfs::kPartitionTokens) return PFS_ERR_UNSUPPORTED;
     if (p.kv_format != PFS_KV_E4M3 && p.kv_format != PFS_KV_E5M2) return PFS_ERR_UNSUPPORTED;
-    if (p.pv_residual != 0 && p.pv_residual != 1) return PFS_ERR_UNSUPPORTED;
-    if (p.pv_residual && p.kv_format != PFS_KV_E4M3) return PFS_ERR_UNSUPPORTED;
+    if (p.pv_mode != PFS_PV_HIGH_RESIDUAL && p.pv_mode != PFS_PV_FP16) return PFS_ERR_UNSUPPORTED;
+    if (p.num_cus < 0 || p.num_cus > 65536) return PFS_ERR_SHAPE;
     if (p.tokens_per_split < 0 || !is_multiple(p.tokens_per_split, p.partition_tokens))
         return PFS_ERR_SHAPE;
 
@@ -145,7 +145,8 @@ int32_t pfs_plan_create(const pfs_problem* pr, pfs_plan** out) {
     }
     if (tps == 0) {
         const int64_t per_cu = pfs::split_workgroups_per_cu(p.head_dim, plan->token_lanes, plan->waves);
-        const int64_t target = (int64_t)pfs::kCUs * per_cu;  // one resident round of workgroups
+        const int64_t cus = p.num_cus > 0 ? p.num_cus : pfs::kDefaultCUs;
+        const int64_t target = cus * per_cu;  // one resident round of workgroups
         const int64_t units = (int64_t)(p.batch > 0 ? p.batch : 1) * p.num_kv_heads * plan->row_blocks;
         int64_t splits = (target + units - 1) / units;
         if (splits < 1) splits = 1;

@@ -12,12 +12,14 @@ import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
 REL_L2_TOL = 1e-3   # relative L2 over every output element of the launch
-MAX_ABS_TOL = 4e-3  # max |y - r| on elements with |r| < 8
-# On |r| >= 8 no FP16 value can be within 4e-3 of every real number (half an
-# FP16 ulp there is >= 2^-8 = 3.9e-3), so those elements are held to one FP16
-# ulp of r (faithful rounding) instead.
-LARGE = 8.0
-
+MAX_ABS_TOL = 4e-3  # max |y - r| on every element with |r| < LARGE
+# Half an FP16 ulp is 2^-9 = 1.95e-3 on [4, 8) and 2^-8 = 3.9e-3 on [8, 16),
+# both below 4e-3, so a correctly rounded output meets the bar there. From
+# |r| >= 16 half an ulp is 7.8e-3: no FP16 value can be within 4e-3 of every
+# real number, so those elements are held to one FP16 ulp of r (faithful
+# rounding) instead. Max abs is reported per band of |r|.
+LARGE = 16.0
+BANDS = ((0.0, 8.0), (8.0, 16.0), (16.0, float("inf")))
 
 def log(msg: str) -> None:
     print(msg, flush=True)
@@ -31,13 +33,14 @@ def device():
     return torch.device("cuda:0")
 
 
-def run(w: W.Workload, *, tokens_per_split: int = 0, tensors=None, out=None, workspace=None, stream=None):
+def run(w: W.Workload, *, tokens_per_split: int = 0, tensors=None, out=None, workspace=None, stream=None,
+        pv_mode: str = "high_residual"):
     """HIP verify on workload w; returns (out tensor, tensors dict)."""
     dev = device()
     t = tensors if tensors is not None else W.device_tensors(w, dev)
     o = pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
                    head_map=t["head_map"], sm_scale=t["sm_scale"], tokens_per_split=tokens_per_split, out=out,
-                   workspace=workspace, stream=stream, kv_format=t.get("kv_format"))
+                   workspace=workspace, stream=stream, kv_format=t.get("kv_format"), pv_mode=pv_mode)
     return o, t
 
 
@@ -59,18 +62,42 @@ def judge(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
     assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output"
     err = np.abs(y - r)
     rel = float(np.linalg.norm(err.ravel()) / max(np.linalg.norm(r.ravel()), 1e-300))
-    small = np.abs(r) < LARGE
+    ar = np.abs(r)
+    small = ar < LARGE
     max_abs_small = float(err[small].max()) if small.any() else 0.0
     max_ulps_large = float((err[~small] / fp16_ulp(r[~small])).max()) if (~small).any() else 0.0
+    bands = {}
+    for lo, hi in BANDS:
+        m = (ar >= lo) & (ar < hi)
+        bands[f"[{lo:g},{hi:g})"] = (float(err[m].max()), int(m.sum())) if m.any() else (0.0, 0)
+    worst = int(np.argmax(err))
     rne = r.astype(np.float16)
     disagree = int((y16.view(np.uint16) != rne.view(np.uint16)).sum())
     rep = dict(rel_l2=rel, max_abs=float(err.max()), max_abs_small=max_abs_small, max_ulps_large=max_ulps_large,
-               fp16_disagreements=disagree, elements=int(r.size))
+               max_abs_by_band=bands, worst_abs_r=float(ar.ravel()[worst]), fp16_disagreements=disagree,
+               elements=int(r.size))
     log(f"[parity] {what}: {rep}")
     assert rel <= REL_L2_TOL, f"{what}: rel L2 {rel}"
-    assert max_abs_small <= MAX_ABS_TOL, f"{what}: max abs {max_abs_small}"
-    assert max_ulps_large <= 1.0, f"{what}: {max_ulps_large} ulp on |r| >= 8"
+    assert max_abs_small <= MAX_ABS_TOL, f"{what}: max abs {max_abs_small} on |r| < {LARGE}"
+    assert max_ulps_large <= 1.0, f"{what}: {max_ulps_large} ulp on |r| >= {LARGE}"
     return rep
+
+def judge_fp16_mode(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
+    """The opt-in single-FP16-probability mode's own bar. Its FP16 rounding
+    of each probability (2^-11 relative) can reach max abs ~4.1e-3 where
+    attention concentrates on keys whose V values nearly cancel, so the mode
+    does not promise the 4e-3 bar: it is held to rel L2 <= 1e-3 and to
+    within two FP16 ulps of r (or 4e-3, whichever is larger) everywhere."""
+    y = y16.astype(np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output"
+    err = np.abs(y - r)
+    rel = float(np.linalg.norm(err.ravel()) / max(np.linalg.norm(r.ravel()), 1e-300))
+    bound = np.maximum(2.0 * fp16_ulp(r), MAX_ABS_TOL)
+    worst = float((err / bound).max())
+    log(f"[parity fp16 mode] {what}: rel_l2={rel} max_abs={float(err.max())} worst/bound={worst}")
+    assert rel <= REL_L2_TOL, f"{what}: rel L2 {rel}"
+    assert worst <= 1.0, f"{what}: an element beyond two FP16 ulps / 4e-3 ({worst})"
+    return dict(rel_l2=rel, max_abs=float(err.max()))
 
 
 def sha(a) -> str:

@@ -108,8 +108,9 @@ def test_valid_problem_plans():
     (dict(partition_tokens=32), "PFS_ERR_UNSUPPORTED"),
     (dict(kv_format=2), "PFS_ERR_UNSUPPORTED"),
     (dict(kv_format=-1), "PFS_ERR_UNSUPPORTED"),
-    (dict(pv_residual=2), "PFS_ERR_UNSUPPORTED"),
-    (dict(pv_residual=1, kv_format=1), "PFS_ERR_UNSUPPORTED"),  # residual P needs E4M3-derived V
+    (dict(pv_mode=2), "PFS_ERR_UNSUPPORTED"),
+    (dict(pv_mode=-1), "PFS_ERR_UNSUPPORTED"),
+    (dict(num_cus=-1), "PFS_ERR_SHAPE"),
     (dict(tokens_per_split=100), "PFS_ERR_SHAPE"),
     (dict(tokens_per_split=16384 + 64), "PFS_ERR_UNSUPPORTED"),  # beyond the split's 1024-tile table
     # 65535 requests x 2 KV heads x 1024 splits of 64 tokens: a split grid beyond 2^31 work-items
@@ -144,11 +145,25 @@ def test_both_kv_formats_plan_identically():
     assert (a.kv_format, b.kv_format) == (0, 1)
 
 
-def test_residual_probabilities_plan_like_the_default():
-    a, b = _lib.Plan(**BASE), _lib.Plan(**dict(BASE, pv_residual=1))
-    assert (a.num_splits, a.tokens_per_split, a.workspace_bytes) == (b.num_splits, b.tokens_per_split,
-                                                                      b.workspace_bytes)
-    assert (a.pv_residual, b.pv_residual) == (0, 1)
+def test_probability_modes_plan_alike():
+    # the probability mode changes only the PV operands: same splits, same workspace,
+    # in either KV format (the residual needs no scaling of V, so E5M2 takes it too)
+    for fmt in (0, 1):
+        a, b = _lib.Plan(**dict(BASE, kv_format=fmt)), _lib.Plan(**dict(BASE, kv_format=fmt, pv_mode=1))
+        assert (a.num_splits, a.tokens_per_split, a.workspace_bytes) == (b.num_splits, b.tokens_per_split,
+                                                                          b.workspace_bytes)
+        assert (a.pv_mode, b.pv_mode) == (0, 1)
+
+
+def test_default_split_length_fills_the_given_compute_units():
+    # 0 means the MI355X's 256; a device with fewer units gets longer splits, one round each way
+    base, same, half = (_lib.Plan(**dict(BASE, num_cus=c)) for c in (0, 256, 128))
+    assert (base.num_splits, base.tokens_per_split) == (same.num_splits, same.tokens_per_split)
+    assert half.tokens_per_split == 2 * base.tokens_per_split
+    assert half.num_splits * 2 == base.num_splits
+    # an explicit split length ignores it
+    a, b = (_lib.Plan(**dict(BASE, tokens_per_split=1024, num_cus=c)) for c in (0, 100))
+    assert (a.num_splits, a.tokens_per_split) == (b.num_splits, b.tokens_per_split)
 
 
 def test_head_major_pool_layout_is_accepted():
@@ -235,7 +250,7 @@ def test_plan_create_null_arguments():
     lib = _lib.load()
     h = ctypes.c_void_p()
     assert lib.pfs_plan_create(None, ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
-    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 0, 64 * 512, 512, 256, 0.0625, None)
+    prob = _lib.PfsProblem(1, 8, 16, 2, 256, 64, 4096, 5000, 64, 0, 0, 0, 0, 64 * 512, 512, 256, 0.0625, None)
     assert lib.pfs_plan_create(ctypes.byref(prob), ctypes.byref(h)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
 
 

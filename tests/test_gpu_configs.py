@@ -75,21 +75,34 @@ def test_config5_sweep_and_fp16_midpoints(q):
         assert np.array_equal(got, exact.astype(np.float16).view(np.uint16)), h
 
 
-def test_determinism_eager_and_graph_replays():
+# (config, q): every named workload, the 8 x 64K batch at each of its q
+DETERMINISM_CASES = [(1, None), (2, None), (3, None), (4, None), (5, 1), (5, 8), (5, 16)]
+
+
+@pytest.mark.parametrize("cfg,q", DETERMINISM_CASES, ids=[f"config{c}" + (f"-q{q}" if q else "")
+                                                          for c, q in DETERMINISM_CASES])
+def test_determinism_eager_and_graph_replays(cfg, q):
+    """Ten eager launches and ten replays of one captured HIP graph, sharing
+    one plan and workspace, give one SHA-256 of the FP16 output (the pages
+    hash outputs across launches: "[Kernel] Finalize the audited TP2 DFlash2
+    31/29 ms endpoint", Test Result; "[Kernel] Preserve DFlash2 sampling
+    precision and repair QUASAR TP2", Test Result). The output buffer is
+    overwritten with a different pattern before every launch and replay."""
     import torch
 
-    w = W.config(2)
+    w = W.config(cfg) if q is None else W.config(cfg, q=q)
+    log(f"[determinism] {w.name}")
     dev = device()
     t = W.device_tensors(w, dev)
     out = torch.empty_like(t["q"])
     plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"],
                          k_pool=t["k_pool"], max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"])
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-    hashes = set()
-    for _ in range(10):
+    hashes = []
+    for k in range(10):
+        out.fill_(float(k) - 4.5)
         run(w, tensors=t, out=out, workspace=ws)
-        hashes.add(sha(to_np(out)))
-    assert len(hashes) == 1
+        hashes.append(sha(to_np(out)))
     eager = to_np(out).copy()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -100,11 +113,14 @@ def test_determinism_eager_and_graph_replays():
     with torch.cuda.graph(g):
         run(w, tensors=t, out=out, workspace=ws)
     for k in range(10):
-        out.fill_(0)
+        out.fill_(float("nan") if k % 2 else 0.0)
         g.replay()
-        y = to_np(out)
-        assert np.array_equal(y.view(np.uint16), eager.view(np.uint16)), f"replay {k}"
-    judge(eager, oracle_ref(w), "config2 eager")
+        hashes.append(sha(to_np(out)))
+    log(f"[determinism] {w.name}: {len(hashes)} outputs, {len(set(hashes))} distinct SHA-256 ({hashes[0][:16]})")
+    assert len(set(hashes)) == 1
+    assert np.all(np.isfinite(eager.astype(np.float64)))
+    if cfg in (1, 2):
+        judge(eager, oracle_ref(w), f"config{cfg} eager")
 
 
 def test_graph_replay_with_changed_lengths_and_pages():

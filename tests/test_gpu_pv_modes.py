@@ -1,8 +1,14 @@
-"""GPU parity of the high/residual probability mode (pv_residual): every
-probability enters the PV product as an FP16 high part plus an FP16 residual
-scaled by 2048, against E4M3 V and V / 2048. Same bar as the default mode
-against the FP64 oracle, bit-identical across launches, and its FP16 outputs
-disagree with the correctly rounded oracle result less often."""
+"""GPU parity of the two probability modes ("[Kernel][SM70] Add opt-in E4M3
+grouped attention with FP32 partials", historical scope list: high/residual
+FP16 PV operands). The default, high_residual, carries every probability into
+the PV product as an FP16 high part plus the FP16 residual p - hi against the
+same V operand (the other GPU tests all run it); the opt-in fp16 mode carries
+the high part alone. Both meet the bar against the FP64 oracle on these
+shapes and are bit-identical across launches; the default's FP16 outputs
+disagree with the correctly rounded oracle result less often. The default is
+held to the full bar (parity.judge); the opt-in mode to its own documented
+one (parity.judge_fp16_mode), since its single FP16 operand can miss max abs
+4e-3 where attention concentrates on nearly cancelling V values."""
 import zlib
 
 import numpy as np
@@ -11,7 +17,7 @@ import pytest
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, to_np
+from parity import device, judge, judge_fp16_mode, log, oracle_ref, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +26,7 @@ def run_mode(w, residual, tokens_per_split=0, tensors=None):
     t = tensors if tensors is not None else W.device_tensors(w, device())
     o = pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
                    head_map=t["head_map"], sm_scale=t["sm_scale"], tokens_per_split=tokens_per_split,
-                   pv_residual=residual)
+                   kv_format=t.get("kv_format"), pv_mode="high_residual" if residual else "fp16")
     return to_np(o), t
 
 
@@ -47,44 +53,49 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("residual", [False, True], ids=["fp16", "high_residual"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_residual_parity(case):
+def test_mode_parity(case, residual):
     name, kw, tps = case
     w = W.build(seed=zlib.crc32(name.encode()) % 1000 + 11, **kw)
-    log(f"[residual] {name} tps={tps}")
-    y, _ = run_mode(w, True, tps)
-    judge(y, oracle_ref(w), "residual " + name)
+    log(f"[pv mode] {name} tps={tps} residual={residual}")
+    y, _ = run_mode(w, residual, tps)
+    (judge if residual else judge_fp16_mode)(y, oracle_ref(w), ("residual " if residual else "fp16 ") + name)
 
 
-def test_residual_is_deterministic_and_differs_from_the_default():
+def test_modes_are_deterministic_and_differ():
     w = W.build(seed=91, batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
                 lengths=[5000, 900])
     a, t = run_mode(w, True)
     b, _ = run_mode(w, True, tensors=t)
     c, _ = run_mode(w, False, tensors=t)
+    d, _ = run_mode(w, False, tensors=t)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(c.view(np.uint16), d.view(np.uint16))
     assert not np.array_equal(a.view(np.uint16), c.view(np.uint16))  # the mode reaches the kernel
 
 
-def test_residual_rejects_e5m2():
-    w = W.build(seed=92, batch=1, q=2, num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=16, lengths=[40],
-                kv_format="e5m2")
-    t = W.device_tensors(w, device())
-    with pytest.raises(pfs.PfsError):
-        pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
-                   kv_format="e5m2", pv_residual=True)
+@pytest.mark.parametrize("residual", [False, True], ids=["fp16", "high_residual"])
+def test_e5m2_in_both_modes(residual):
+    # the residual needs no scaling of V, so E5M2 pools take it as well
+    w = W.build(seed=92, batch=2, q=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                lengths=[1500, 77], kv_format="e5m2", outlier_frac=0.02)
+    y, _ = run_mode(w, residual, 256)
+    (judge if residual else judge_fp16_mode)(y, oracle_ref(w), ("residual" if residual else "fp16") + " e5m2")
 
 
 @pytest.mark.parametrize("cfg,q", [(2, None), (3, None), (5, 8)])
-def test_residual_full_size_and_disagreements(cfg, q):
-    """Full-size workloads, every element: the residual mode meets the bar and
-    its FP16 outputs disagree with RNE(oracle) no more often than the default."""
+def test_full_size_disagreements(cfg, q):
+    """Full-size workloads, every element: both modes meet the bar, and the
+    high/residual default's FP16 outputs disagree with RNE(oracle) no more
+    often than the fp16 mode's."""
     w = W.config(cfg) if q is None else W.config(cfg, q=q)
-    log(f"[residual] config {cfg} ({w.name})")
+    log(f"[pv mode] config {cfg} ({w.name})")
     r = oracle_ref(w)
     y1, t = run_mode(w, False)
     y2, _ = run_mode(w, True, tensors=t)
     judge(y2, r, f"residual {w.name}")
+    judge_fp16_mode(y1, r, f"fp16 {w.name}")
     d1, d2 = disagreements(y1, r), disagreements(y2, r)
-    log(f"[residual] {w.name}: FP16 disagreements with RNE(oracle): default {d1}, residual {d2} of {r.size}")
+    log(f"[pv mode] {w.name}: FP16 disagreements with RNE(oracle): fp16 {d1}, high_residual {d2} of {r.size}")
     assert d2 <= d1

@@ -418,6 +418,36 @@ def test_kv_append_writes_exactly_the_draft_slots(kv_format):
     assert np.array_equal(view_k[~touched], old_k[~touched])
 
 
+def test_kv_append_feeds_exactly_the_causal_window_of_verify():
+    """Append placement tied to verify's causal mask by behaviour alone (no
+    slot formula restated): draft row i's K/V become visible to verify rows
+    i and later and to no earlier row. Changing the appended V of draft row j
+    changes exactly the outputs of rows i >= j; changing only a non-draft
+    (history) token changes every row that sees it."""
+    w = W.build(seed=63, batch=2, q=5, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                lengths=[70, 5])
+    rng = np.random.default_rng(64)
+    kn = rng.normal(0, 2, (2, 5, 2, 64)).astype(np.float16)
+    vn = rng.normal(0, 2, (2, 5, 2, 64)).astype(np.float16)
+
+    def verify_after(kk, vv):
+        kp, vp = oracle.kv_append(w, kk, vv)
+        wk = w.copy()
+        wk.k_pool, wk.v_pool = kp, vp
+        return oracle.verify(wk)
+
+    base = verify_after(kn, vn)
+    assert np.all(np.isfinite(base))
+    for j in range(w.q):
+        v2 = vn.copy()
+        v2[:, j] = (v2[:, j].astype(np.float32) + 1.0).astype(np.float16)
+        out = verify_after(kn, v2)
+        for b in range(w.batch):
+            for i in range(w.q):
+                changed = not np.array_equal(out[b, i], base[b, i])
+                assert changed == (i >= j), (b, i, j)
+
+
 # ---- the scaled E4M3 -> FP16 bridge ----
 
 def test_fp16_rne_matches_numpy_double_to_half():
