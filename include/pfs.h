@@ -247,6 +247,30 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
                            pfs_stream_t stream);
 
 /*
+ * pfs_verify without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The split partials live in a device
+ * array inside the library instead (one per GPU, pfs_noalloc_scratch_bytes()
+ * = 128 MiB, held from the first call on that GPU until the process ends);
+ * the kernels, the arithmetic and therefore the output bits are those of
+ * pfs_verify with the same plan. The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine (its first call on a device looks
+ * the array's address up once). A plan whose pfs_plan_workspace_bytes()
+ * exceeds the array is refused with PFS_ERR_WORKSPACE. Calls on one GPU
+ * share the array: calls that overlap in time on one GPU (different
+ * streams, or host threads without stream order) race and give undefined
+ * outputs; stream-ordered calls are safe. Other arguments and errors as for
+ * pfs_verify.
+ */
+int32_t pfs_verify_noalloc(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_pool,
+                           const uint8_t* v_pool, const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* live_len, void* out_fp16,
+                           pfs_stream_t stream);
+
+/* Size in bytes of the per-GPU device array pfs_verify_noalloc uses. */
+int64_t pfs_noalloc_scratch_bytes(void);
+
+/*
  * Paged FP8 -> FP16 bridge: the dequant-on-load path as a call of its own,
  * turning paged E4M3 (or E5M2) bytes into a dense FP16 array
  * ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32 partials",

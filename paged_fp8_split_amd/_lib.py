@@ -118,6 +118,10 @@ def load():
     lib.pfs_dequant_paged.argtypes = [P] * 7
     lib.pfs_kv_append.restype = c.c_int32
     lib.pfs_kv_append.argtypes = [P] * 10
+    lib.pfs_verify_noalloc.restype = c.c_int32
+    lib.pfs_verify_noalloc.argtypes = [P] * 10
+    lib.pfs_noalloc_scratch_bytes.restype = c.c_int64
+    lib.pfs_noalloc_scratch_bytes.argtypes = []
     _lib = lib
     return lib
 
@@ -185,6 +189,21 @@ def verify(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table, live_le
                         int(workspace.numel() * workspace.element_size()), _stream_handle(q.device, stream))
     if st != 0:
         raise PfsError(st, "pfs_verify")
+
+
+def verify_noalloc(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, out,
+                   stream=None) -> None:
+    """pfs_verify_noalloc: pfs_verify with the partials in the library's
+    per-GPU device array (no workspace, nothing allocated)."""
+    st = plan._lib.pfs_verify_noalloc(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                      _ptr(v_scale), _ptr(block_table), _ptr(live_len), _ptr(out),
+                                      _stream_handle(q.device, stream))
+    if st != 0:
+        raise PfsError(st, "pfs_verify_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().pfs_noalloc_scratch_bytes())
 
 
 def verify_split(plan: Plan, q, k_pool, v_pool, k_scale, block_table, live_len, workspace, stream=None) -> None:

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpfs.so")
 SOURCES = [os.path.join(CSRC, "pfs_plan.cpp"), os.path.join(CSRC, "pfs_kernels.hip"),
-           os.path.join(CSRC, "pfs_codec.hip")]
+           os.path.join(CSRC, "pfs_codec.hip"), os.path.join(CSRC, "pfs_noalloc.hip")]
 ARCH = "gfx950"
 
 

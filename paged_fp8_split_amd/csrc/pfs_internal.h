@@ -19,6 +19,9 @@ constexpr int max_row_tiles(int head_dim) { return head_dim >= 256 ? 1 : (head_d
 constexpr int kTileTableEntries = 1024;
 constexpr int kMaxTokensPerSplit = 16 * kTileTableEntries;
 constexpr int kDefaultCUs = 256;  // MI355X compute units: the default split length fills them
+// Size of the device array that holds the split partials of pfs_verify_noalloc
+// (per GPU, for the life of the process).
+constexpr int64_t kNoallocScratchBytes = 128ll << 20;
 
 // A split workgroup has W = RG * TP waves: RG row groups (RT row tiles each)
 // times TP token lanes; a stage holds TP 32-token steps of K and V bytes.

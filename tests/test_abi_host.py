@@ -27,9 +27,19 @@ def test_library_exports_every_declared_symbol():
         "pfs_abi_version", "pfs_dequant_paged", "pfs_kv_append", "pfs_plan_create", "pfs_plan_destroy",
         "pfs_plan_num_splits",
         "pfs_plan_tokens_per_split", "pfs_plan_workspace_bytes", "pfs_status_string", "pfs_verify",
-        "pfs_verify_combine", "pfs_verify_split"])
+        "pfs_verify_combine", "pfs_verify_split", "pfs_verify_noalloc", "pfs_noalloc_scratch_bytes"])
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_noalloc_scratch_size_and_refusals_without_a_gpu():
+    # the stated size, and the host-side checks that run before any HIP call
+    assert _lib.noalloc_scratch_bytes() == 128 << 20
+    lib = _lib.load()
+    assert lib.pfs_verify_noalloc(None, *([None] * 9)) == _lib.STATUS_CODE["PFS_ERR_NULL"]
+    big = _lib.Plan(**dict(BASE, batch=64))  # 64 requests x 262,144 tokens: far beyond 128 MiB of partials
+    assert big.workspace_bytes > _lib.noalloc_scratch_bytes()
+    assert lib.pfs_verify_noalloc(big.handle, *([None] * 9)) == _lib.STATUS_CODE["PFS_ERR_WORKSPACE"]
 
 
 def test_abi_version_and_status_strings():
