@@ -157,13 +157,16 @@ def codec_timing(w, t, dev, evict, reps: int = 20) -> dict:
         for k in range(reps + 3):
             if scrub:
                 evict()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            T = timer()
+            e0, e1 = T.event(), T.event()
+            stream = torch.cuda.current_stream()
+            T.record(e0, stream)
             fn()
-            e1.record()
+            T.record(e1, stream)
             torch.cuda.synchronize()
             if k >= 3:
-                ms.append(e0.elapsed_time(e1))
+                ms.append(T.elapsed_ms(e0, e1))
+            T.destroy([e0, e1])
         return float(np.median(ms)) * 1e3
 
     # the append is a few microseconds of GPU work: time a graph of `chain`
@@ -195,13 +198,81 @@ def codec_timing(w, t, dev, evict, reps: int = 20) -> dict:
     }
 
 
+class HipTimer:
+    """Timing events recorded on a HIP stream through the HIP runtime that
+    torch itself loaded, created with hipEventDisableSystemFence: recording
+    such an event skips the system-scope cache write-back and invalidate that
+    a default event performs (HIP's documentation offers the flag for timing
+    events for exactly that reason). A default event between two kernels
+    leaves the GPU idle for about 5.5 us on this stack (rocprofv3 kernel
+    trace: scrub end -> split start is 0 without an event, 5.5 us with one),
+    which would be counted inside the timed step."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime (libamdhip64.so) is not loaded")
+        self.hip = ctypes.CDLL(path)
+        self.c = ctypes
+        for fn, args in (("hipEventCreateWithFlags", [ctypes.c_void_p, ctypes.c_uint]),
+                         ("hipEventRecord", [ctypes.c_void_p, ctypes.c_void_p]),
+                         ("hipEventSynchronize", [ctypes.c_void_p]),
+                         ("hipEventElapsedTime", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                         ("hipEventDestroy", [ctypes.c_void_p])):
+            getattr(self.hip, fn).argtypes = args
+            getattr(self.hip, fn).restype = ctypes.c_int
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError {rc}")
+
+    def event(self):
+        ev = self.c.c_void_p()
+        self._ok(self.hip.hipEventCreateWithFlags(self.c.byref(ev), self.FLAGS), "hipEventCreateWithFlags")
+        return ev
+
+    def record(self, ev, stream):
+        self._ok(self.hip.hipEventRecord(ev, self.c.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def elapsed_ms(self, a, b) -> float:
+        self._ok(self.hip.hipEventSynchronize(b), "hipEventSynchronize")
+        ms = self.c.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.c.byref(ms), a, b), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for ev in evs:
+            self.hip.hipEventDestroy(ev)
+
+
+_TIMER = None
+
+
+def timer() -> HipTimer:
+    global _TIMER
+    if _TIMER is None:
+        _TIMER = HipTimer()
+    return _TIMER
+
+
 def time_steps(split, combine, evict, stream, steps: int, warmup: int, mid_event: bool):
     """Warm up, then time `steps` scrubbed split + combine steps with HIP
-    events on `stream`. With `mid_event` an event between the two kernels
-    also splits each step into its kernels (that event delays the combine's
-    start by a few microseconds, so the step itself is timed without it).
-    Returns (split_ms, combine_ms, step_ms, wall_s); the first two are None
-    without `mid_event`."""
+    events (HipTimer) on `stream`. With `mid_event` an event between the two
+    kernels also splits each step into its kernels (the step itself is timed
+    without it). Returns (split_ms, combine_ms, step_ms, wall_s); the first
+    two are None without `mid_event`."""
     import numpy as np
     import torch
 
@@ -211,31 +282,31 @@ def time_steps(split, combine, evict, stream, steps: int, warmup: int, mid_event
         combine()
     torch.cuda.synchronize()
     note("warmup done; timing")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    T = timer()
+    evs = [[T.event() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for k in range(steps):
         evict()
-        evs[k][0].record(stream)
+        T.record(evs[k][0], stream)
         split()
         if mid_event:
-            evs[k][1].record(stream)
+            T.record(evs[k][1], stream)
         combine()
-        evs[k][2].record(stream)
+        T.record(evs[k][2], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
-    if not mid_event:
-        return None, None, step_ms, wall
-    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([T.elapsed_ms(e[0], e[2]) for e in evs])
+    split_ms = np.array([T.elapsed_ms(e[0], e[1]) for e in evs]) if mid_event else None
+    comb_ms = np.array([T.elapsed_ms(e[1], e[2]) for e in evs]) if mid_event else None
+    T.destroy([x for e in evs for x in e])
     return split_ms, comb_ms, step_ms, wall
 
 
 def time_graph(graph, evict, stream, steps: int, warmup: int):
     """Warm up, then time `steps` replays of `graph`, each after an untimed
-    scrub, with HIP events around each replay on `stream`. Returns
-    (step_ms, wall_s)."""
+    scrub, with HIP events (HipTimer) on `stream` around each replay: the
+    graph's launch is inside the interval. Returns (step_ms, wall_s)."""
     import numpy as np
     import torch
 
@@ -243,17 +314,20 @@ def time_graph(graph, evict, stream, steps: int, warmup: int):
         evict()
         graph.replay()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    T = timer()
+    evs = [[T.event() for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for k in range(steps):
         evict()
-        evs[k][0].record(stream)
+        T.record(evs[k][0], stream)
         graph.replay()
-        evs[k][1].record(stream)
+        T.record(evs[k][1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    return np.array([e[0].elapsed_time(e[1]) for e in evs]), wall
+    res = np.array([T.elapsed_ms(e[0], e[1]) for e in evs])
+    T.destroy([x for e in evs for x in e])
+    return res, wall
 
 
 def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3",
@@ -387,6 +461,9 @@ def main() -> int:
     ap.add_argument("--tokens-per-split", type=int, default=0)
     ap.add_argument("--q", type=int, default=None,
                     help="draft rows per request (the 8 x 64K batch also runs at q = 1 and q = 16)")
+    ap.add_argument("--pv-mode", default="high_residual", choices=["high_residual", "fp16"],
+                    help="probability operands of the timed line (default high_residual)")
+    ap.add_argument("--kv-format", default="e4m3", choices=["e4m3", "e5m2"], help="KV byte format of the timed line")
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the Infinity Cache between steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -421,11 +498,11 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     note(f"generating workload config {args.config}")
-    w = W.config(args.config, q=args.q)
+    w = W.config(args.config, q=args.q, kv_format=args.kv_format)
     t = W.device_tensors(w, dev)
     plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
                          max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"],
-                         tokens_per_split=args.tokens_per_split)
+                         tokens_per_split=args.tokens_per_split, kv_format=args.kv_format, pv_mode=args.pv_mode)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["q"])
     scrub = None if args.no_scrub else torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read only
@@ -446,7 +523,8 @@ def main() -> int:
 
     note(f"plan: {plan.num_splits} splits x {plan.tokens_per_split} tokens, workspace {plan.workspace_bytes} B, "
          f"{plan.num_cus} CUs")
-    # the headline: the step captured once as a HIP graph, replayed after each scrub
+    # the headline: the step captured once as a HIP graph, replayed after
+    # each scrub, HIP events (hipEventDisableSystemFence) around each replay
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         _lib.verify(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
@@ -464,14 +542,27 @@ def main() -> int:
     split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, args.steps, 0, mid_event=True)
 
     # the graph replayed back to back without scrubs (cache-warm: context only)
-    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    T = timer()
+    ga, gb = T.event(), T.event()
     reps = 50
-    ga.record()
+    T.record(ga, stream)
     for _ in range(reps):
         g.replay()
-    gb.record()
+    T.record(gb, stream)
     torch.cuda.synchronize()
-    graph_warm_ms = ga.elapsed_time(gb) / reps
+    graph_warm_ms = T.elapsed_ms(ga, gb) / reps
+    T.destroy([ga, gb])
+    # context: the same scrubbed replays timed with torch's default events,
+    # whose system-scope fence idles the GPU before the step starts
+    dflt = []
+    for _ in range(10):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dflt.append(e0.elapsed_time(e1))
 
     kv = w.kv_bytes()
     mean_ms = float(graph_step_ms.mean())
@@ -480,7 +571,8 @@ def main() -> int:
     split_bytes = split_algorithmic_bytes(w, plan)
     split_mean_ms = float(split_ms.mean())
     achieved = split_bytes / (split_mean_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(args.config)
+    default_line = args.pv_mode == "high_residual" and args.kv_format == "e4m3" and args.tokens_per_split == 0
+    traffic = traffic_from_profiles(args.config) if default_line else None
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -492,13 +584,15 @@ def main() -> int:
         "us_per_step": round(mean_ms * 1e3, 2),
         "us_per_step_p10_p50_p90": [round(float(np.percentile(graph_step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "kv_pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "timing": "HIP-graph replay of split + combine, events around each replay, Infinity Cache scrubbed before each",
+        "timing": "HIP-graph replay of split + combine, HIP events (hipEventDisableSystemFence) around each replay on "
+                  "its stream (the graph launch inside the interval), Infinity Cache scrubbed before each replay",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "precision": "E4M3 KV bytes; FP16 MFMA operands (probabilities as FP16 high + FP16 residual); FP32 "
-                     "accumulation and split partials; FP16 output",
+        "precision": f"{args.kv_format.upper()} KV bytes; FP16 MFMA operands (probabilities as "
+                     + ("FP16 high + FP16 residual" if args.pv_mode == "high_residual" else "one FP16 operand")
+                     + "); FP32 accumulation and split partials; FP16 output",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -513,7 +607,8 @@ def main() -> int:
             "tokens_per_split": plan.tokens_per_split,
             "num_splits": plan.num_splits,
             "num_cus": plan.num_cus,
-            "pv_mode": "high_residual",
+            "pv_mode": args.pv_mode,
+            "kv_format": args.kv_format,
             "kv_bytes": kv,
             "infinity_cache_scrub": scrub is not None,
         },
@@ -531,12 +626,13 @@ def main() -> int:
             "algorithmic_bytes_per_launch": split_bytes,
             "mean_launch_us": round(split_mean_ms * 1e3, 2),
         },
-        "mfma": mfma_report(w, split_mean_ms, args.config),
+        "mfma": mfma_report(w, split_mean_ms, args.config if default_line else None),
         "us_per_step_eager": round(eager_ms * 1e3, 2),
         "kv_pct_of_peak_hbm_eager": round(100.0 * kv / (eager_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "eager_output_matches_graph": bool(eager_same),
         "combine_us": round(float(comb_ms.mean()) * 1e3, 2),
         "graph_replay_cache_warm_us": round(graph_warm_ms * 1e3, 2),
+        "us_per_step_graph_default_events": round(float(np.mean(dflt)) * 1e3, 2),
         "timed_loop_wall_s": round(wall, 4),
         "output_sha256": out_sha,
         "kernel_source_sha": kernel_source_sha(),
