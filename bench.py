@@ -373,6 +373,87 @@ def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m
     return res
 
 
+def ceiling(args, dev) -> dict:
+    """Read-bandwidth probes (libpfs_probe.so) on the timed workload's pools:
+    the live K and V bytes of the step, read in the split kernel's units
+    (one 512-thread workgroup per (split, KV head), pages resolved through
+    the block table) with no arithmetic, once with register loads and once
+    straight into LDS through the split kernel's pipeline of stages; then the
+    same number of bytes read from one flat buffer; the split kernel alone
+    for comparison. Each launch after the read-only scrub, HIP events
+    (HipTimer) around it; bytes = the live K and V bytes."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import paged_fp8_split_amd as pfs
+    from paged_fp8_split_amd import _lib
+    from paged_fp8_split_amd import workloads as W
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_fp8_split_amd", "libpfs_probe.so"))
+    lib.pfs_probe_paged.restype = ctypes.c_int32
+    lib.pfs_probe_paged.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + \
+        [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 2
+    lib.pfs_probe_flat.restype = ctypes.c_int32
+    lib.pfs_probe_flat.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    w = W.config(args.config, q=args.q)
+    if w.batch != 1:
+        raise SystemExit("--ceiling probes one request (configs 1, 2 and 3)")
+    t = W.device_tensors(w, dev)
+    plan = pfs.make_plan(batch=1, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"], k_pool=t["k_pool"],
+                         max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"])
+    L = int(w.live_len[0])
+    kv = w.kv_bytes()
+    grid = plan.num_splits * w.num_kv_heads
+    sink = torch.empty(grid * 512, dtype=torch.int32, device=dev)
+    flat = torch.ones(kv // 4, dtype=torch.int32, device=dev)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    scrub_sink = torch.empty((), dtype=torch.float32, device=dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    T = timer()
+
+    def paged(mode):
+        rc = lib.pfs_probe_paged(mode, t["k_pool"].data_ptr(), t["v_pool"].data_ptr(), t["block_table"].data_ptr(),
+                                 w.page_stride, w.token_stride, w.head_stride, w.page_size, w.head_dim,
+                                 w.num_kv_heads, plan.tokens_per_split, plan.num_splits, L, sink.data_ptr(), sp)
+        assert rc == 0, rc
+
+    def flat_read():
+        assert lib.pfs_probe_flat(flat.data_ptr(), kv, grid, sink.data_ptr(), sp) == 0
+
+    def split():
+        _lib.verify_split(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["block_table"], t["live_len"], ws,
+                          stream)
+
+    cases = {"paged_register_loads": lambda: paged(0), "paged_direct_to_lds": lambda: paged(1),
+             "flat_register_loads": flat_read, "split_kernel": split}
+    times = {k: [] for k in cases}
+    for fn in cases.values():  # warm up every path
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    for r in range(args.steps):  # interleaved, every launch after a scrub
+        for name, fn in cases.items():
+            torch.sum(scrub, 0, out=scrub_sink)
+            e0, e1 = T.event(), T.event()
+            T.record(e0, stream)
+            fn()
+            T.record(e1, stream)
+            times[name].append(T.elapsed_ms(e0, e1))
+            T.destroy([e0, e1])
+    note(f"ceiling: {args.steps} interleaved rounds")
+    res = {"workload": w.name, "kv_bytes": kv, "workgroups": grid, "tokens_per_split": plan.tokens_per_split}
+    for name, ms in times.items():
+        ms = np.array(ms)
+        res[name] = {"us_mean": round(float(ms.mean()) * 1e3, 2), "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                     "kv_TBps": round(kv / (float(ms.mean()) * 1e-3) / 1e12, 3),
+                     "frac_of_8TBps": round(kv / (float(ms.mean()) * 1e-3) / 1e12 / 8.0, 4)}
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -469,6 +550,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the residual-probability and E5M2 variants of the workload")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only run the read-bandwidth probes (libpfs_probe.so) on the workload's pools and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (to scale HBM byte counters) and exit")
     args = ap.parse_args()
@@ -497,6 +580,9 @@ def main() -> int:
     from paged_fp8_split_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.ceiling:
+        print(json.dumps({"ceiling": ceiling(args, dev)}), flush=True)
+        return 0
     note(f"generating workload config {args.config}")
     w = W.config(args.config, q=args.q, kv_format=args.kv_format)
     t = W.device_tensors(w, dev)

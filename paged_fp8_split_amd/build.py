@@ -19,6 +19,9 @@ LIB = os.path.join(HERE, "libpfs.so")
 SOURCES = [os.path.join(CSRC, "pfs_plan.cpp"), os.path.join(CSRC, "pfs_kernels.hip"),
            os.path.join(CSRC, "pfs_codec.hip"), os.path.join(CSRC, "pfs_noalloc.hip")]
 ARCH = "gfx950"
+# read-bandwidth probes for bench.py --ceiling (measurement only; libpfs does not use them)
+PROBE_SOURCES = [os.path.join(CSRC, "pfs_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libpfs_probe.so")
 
 
 def hipcc() -> str:
@@ -44,9 +47,9 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *flags(), "-o", tmp, *SOURCES]
+def _compile(sources, out, verbose):
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *flags(), "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,8 +59,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libpfs.so and the probe library libpfs_probe.so; returns the
+    path of libpfs.so."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
