@@ -229,10 +229,12 @@ int32_t pfs_verify(const pfs_plan* plan, const void* q_fp16, const uint8_t* k_po
  * fixed by the plan alone (never by timing or device data), so repeated
  * calls give bit-identical outputs:
  *   - plans with at most 32 splits: splits 0, 1, 2, ... one after another;
- *   - more splits: the S splits are cut into 8 contiguous blocks of
- *     ceil(S / 8); each block is summed in ascending split order, then the
- *     8 block sums are combined in a fixed pairwise tree, (0+1), (2+3),
- *     (4+5), (6+7), then (01+23), (45+67), then (0123+4567).
+ *   - more splits: the S splits are cut into NB contiguous blocks of
+ *     ceil(S / NB) splits (NB = 16 at head_dim 128 and 256, 32 at 64);
+ *     each block is summed in ascending split order, then the NB block
+ *     sums are combined in a fixed pairwise tree: (0+1), (2+3), ..., then
+ *     (01+23), (45+67), ..., and so on up to one sum, the lower blocks
+ *     always the left operand.
  * Before each addition the two operands are rescaled to their common
  * maximum. pfs_verify_split followed by pfs_verify_combine on the same
  * stream, plan and workspace is exactly pfs_verify. Arguments and errors as

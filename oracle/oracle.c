@@ -467,8 +467,8 @@ uint32_t oracle_fp16_rne(double v) {
 
 /*
  * Paged E4M3 -> FP16 bridge ("[Kernel][SM70] Add opt-in E4M3 grouped
- * attention with FP32 partials", Scope list: the E4M3 paged-to-FP16 bridge
- * API): out[b][t][g][d] = FP16 bits of dec(byte) * scale[g] rounded once to
+ * attention with FP32 partials", Scope list: a standalone call that turns
+ * the paged FP8 cache into FP16): out[b][t][g][d] = FP16 bits of dec(byte) * scale[g] rounded once to
  * nearest even for t < live_len[b], +0.0 beyond, with dec the decoder of
  * kv_format (0 = E4M3FN, 1 = E5M2). scale == NULL means 1.
  * out is [batch, max_pages_per_row * page_size, num_kv_heads, head_dim].

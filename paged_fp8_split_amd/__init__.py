@@ -102,7 +102,7 @@ def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_
 def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_map: Optional[Sequence[int]] = None,
            sm_scale: Optional[float] = None, partition_tokens: int = 64, tokens_per_split: int = 0, out=None,
            workspace=None, stream=None, plan=None, kv_format: Optional[str] = None,
-           pv_mode: str = "high_residual"):
+           pv_mode: str = "high_residual", noalloc: bool = False):
     """Verify attention of q draft rows per request over a paged FP8 KV cache.
 
     q            [B, q, Hq, D] float16, contiguous, on the GPU
@@ -119,6 +119,10 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     block_table  [B, max_pages_per_row] int32
     live_len     [B] int32, draft tokens included
     head_map     query head -> KV head (default h // (Hq // Hkv))
+    noalloc      keep the split partials in the library's per-GPU device
+                 array (pfs_verify_noalloc) instead of a workspace; with
+                 ``out`` given, nothing is allocated. Calls that overlap on
+                 one GPU share that array and must not run concurrently.
     Returns out [B, q, Hq, D] float16. No host synchronization.
     """
     from . import _lib
@@ -147,6 +151,11 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
             raise ValueError(f"{name} must be a contiguous {dt} tensor")
     if out is None:
         out = torch.empty_like(q)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace: the partials live in the library's device array")
+        _lib.verify_noalloc(plan, q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, out, stream)
+        return out
     if workspace is None:
         workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     _lib.verify(plan, q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, out, workspace, stream)

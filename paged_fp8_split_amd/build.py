@@ -8,6 +8,7 @@ warns that it does not know that feature, which is harmless.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -47,7 +48,38 @@ def flags() -> list:
     ]
 
 
+def _digest(sources) -> str:
+    """SHA-256 over the compile flags, the sources and every header they can
+    include (csrc/*.h and include/*.h), so an edit anywhere shows up."""
+    inc = os.path.join(os.path.dirname(HERE), "include")
+    headers = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h"))
+    headers += sorted(os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h"))
+    h = hashlib.sha256(" ".join(flags()).encode())
+    for path in list(sources) + headers:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _stamp(out) -> str:
+    return out + ".srcsha"
+
+
+def stale() -> bool:
+    """True if either library is missing or was built from other sources than
+    the tree holds now (content digest, not file times, so a copied tree whose
+    build is current stays current)."""
+    for sources, out in ((SOURCES, LIB), (PROBE_SOURCES, PROBE_LIB)):
+        if not os.path.exists(out) or not os.path.exists(_stamp(out)):
+            return True
+        with open(_stamp(out)) as f:
+            if f.read().strip() != _digest(sources):
+                return True
+    return False
+
+
 def _compile(sources, out, verbose):
+    digest = _digest(sources)
     tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), *flags(), "-o", tmp, *sources]
     if verbose:
@@ -60,6 +92,8 @@ def _compile(sources, out, verbose):
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, out)
+    with open(_stamp(out), "w") as f:
+        f.write(digest + "\n")
     return out
 
 

@@ -9,8 +9,8 @@
 //                       scaling)
 //   pfs_bridge_kernel   paged FP8 -> dense FP16, optionally scaled
 //                       ("[Kernel][SM70] Add opt-in E4M3 grouped attention
-//                       with FP32 partials", Scope list: the explicit E4M3
-//                       paged-to-FP16 bridge API)
+//                       with FP32 partials", Scope list: a call of its own
+//                       that turns the paged FP8 cache into FP16)
 //
 // Both kernels exist for the two KV formats (template parameter FMT): OCP
 // E4M3FN, the method's format, and E5M2, the explicit alternative ("[Bugfix]

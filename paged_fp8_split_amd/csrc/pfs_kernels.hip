@@ -991,38 +991,56 @@ __device__ __forceinline__ void select_splits(int s0, int s_lim, float2 (&v)[N],
     }
 }
 
-// Many splits: one workgroup of NW waves per (request, KV head, row, column
-// slice); each wave owns 32 columns of the row. Lane (sl, cg) = (lane / 8,
-// lane % 8) owns columns 4 cg .. 4 cg + 3 of its wave's 32 and split block sl.
-// The plan's splits are cut into 8 contiguous blocks of C = ceil(S / 8)
-// splits; lane sl folds the visible splits of block sl in ascending order,
-// kCombineRound at a time with their loads issued together (the first round
-// before the live length has arrived: slots past the visible splits are read
-// and selected out). The 8 block states are then merged across the wave's
-// lanes (cross-lane permutes, no LDS) in a fixed pairwise tree: blocks (0,1),
-// (2,3), (4,5), (6,7), then (01,23), (45,67), then (0123,4567), the lower
-// blocks always the left operand. One IEEE division, one RNE to FP16.
-constexpr int kCombineSplitLanes = 8;
-constexpr int kCombineRound = 16;
+// Many splits: one workgroup of NW = 8 waves per (request, KV head, row,
+// column slice of 4 CGW columns; CGW = 32, or 16 at head_dim 64). Lane
+// (sl, cg) = (lane / CGW, lane % CGW) of wave w owns columns 4 cg .. 4 cg + 3
+// of the slice and split block SL w + sl (SL = 64 / CGW), so one load
+// instruction of a wave reads SL runs of 16 CGW contiguous bytes (512 B at
+// head_dim 128 and 256): long runs, not the number of waves, set how fast the
+// one burst of partial reads completes. The plan's splits are cut into
+// SL NW contiguous blocks of C = ceil(S / (SL NW)) splits (16 blocks, 32 at
+// head_dim 64); a lane folds its block in ascending order, kCombineRound
+// splits at a time with their loads issued together (the first round before
+// the live length has arrived: slots past the visible splits are read and
+// selected out). The block states are then merged in a fixed pairwise tree:
+// inside each wave by cross-lane permutes over the lane bits that select sl,
+// then across the waves through LDS, (w0, w1), (w2, w3), ..., then pairs of
+// pairs; the lower blocks are always the left operand. One IEEE division, one
+// RNE to FP16.
+constexpr int kCombineWaves = 8;  // waves per workgroup
+constexpr int kCombineRound = 8;
 constexpr int kCombineRowSplits = 32;  // at most this many splits: pfs_combine_rows_kernel
+
+__host__ __device__ constexpr int combine_cgw(int d) { return d / 4 < 32 ? d / 4 : 32; }
 
 __device__ __forceinline__ float lane_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Merges two fold states, l the lower split blocks: the larger maximum, each
+// side rescaled by its own factor (0 for an empty side).
+__device__ __forceinline__ FoldState merge_states(const FoldState& l, const FoldState& r) {
+    FoldState o;
+    o.M = fmaxf(l.M, r.M);
+    const float fl = (l.M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l.M - o.M);
+    const float fr = (r.M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(r.M - o.M);
+    o.lw = fl * l.lw + fr * r.lw;
+    o.acc = fl * l.acc + fr * r.acc;
+    return o;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
-    constexpr int SL = kCombineSplitLanes;
-    constexpr int CGW = 64 / SL;                    // 4-column groups per wave (32 columns)
-    constexpr int NW = D / 32 < 4 ? D / 32 : 4;     // waves per workgroup
-    constexpr int COLS = 32 * NW;                   // columns per workgroup
-    constexpr int SLICES = D / COLS;
+__global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const CombineArgs a) {
+    constexpr int CGW = combine_cgw(D);  // 4-column groups per wave
+    constexpr int SL = 64 / CGW;         // split blocks per wave
+    constexpr int NW = kCombineWaves;
+    constexpr int SLICES = D / (4 * CGW);
     constexpr int R = kCombineRound;
-    static_assert(SLICES * COLS == D, "combine slice");
+    __shared__ float part[NW - 1][CGW][6];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sl = lane / CGW;
     const int cg = lane % CGW;
     const int r = blockIdx.x / SLICES;
-    const int col0 = (blockIdx.x % SLICES) * COLS + 32 * wave + 4 * cg;
+    const int col0 = (blockIdx.x % SLICES) * 4 * CGW + 4 * cg;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
     const int i = r / a.group;
@@ -1030,8 +1048,8 @@ __global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
     _Float16* dst = a.out + (((int64_t)b * a.q + i) * a.num_q_heads + h) * D + col0;
     const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;  // between splits
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
-    const int C = (a.num_splits + SL - 1) / SL;
-    const int s_begin = sl * C;
+    const int C = (a.num_splits + SL * NW - 1) / (SL * NW);
+    const int s_begin = (wave * SL + sl) * C;
     const int s_end = min(s_begin + C, a.num_splits);
 
     const int32_t L_raw = a.live_len[b];
@@ -1050,26 +1068,41 @@ __global__ __launch_bounds__(256) void pfs_combine_kernel(const CombineArgs a) {
         select_splits<R>(s0, s_lim, v, x);
         fold_splits<R>(st, v, x);
     }
-    // pairwise tree over the 8 blocks (lane bits 3, 4, 5 select the block)
+    // pairwise tree over the wave's SL blocks (the lane bits above cg)
 #pragma unroll
     for (int bit = CGW; bit < 64; bit <<= 1) {
-        const float oM = lane_xor(st.M, bit);
-        const float ol = lane_xor(st.lw, bit);
-        f32x4 oa;
+        FoldState o;
+        o.M = lane_xor(st.M, bit);
+        o.lw = lane_xor(st.lw, bit);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) oa[c] = lane_xor(st.acc[c], bit);
-        const bool upper = (lane & bit) != 0;  // this lane holds the right operand
-        const float Ml = upper ? oM : st.M, Mr = upper ? st.M : oM;
-        const float ll = upper ? ol : st.lw, lr = upper ? st.lw : ol;
-        const f32x4 al = upper ? oa : st.acc, ar = upper ? st.acc : oa;
-        const float Mg = fmaxf(Ml, Mr);
-        const float fl = (Ml == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Ml - Mg);
-        const float fr = (Mr == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Mr - Mg);
-        st.M = Mg;
-        st.lw = fl * ll + fr * lr;
-        st.acc = fl * al + fr * ar;
+        for (int c = 0; c < 4; ++c) o.acc[c] = lane_xor(st.acc[c], bit);
+        st = (lane & bit) ? merge_states(o, st) : merge_states(st, o);
     }
-    if (sl != 0) return;
+    // then the waves: lanes sl == 0 of waves 1.. hand their states to wave 0
+    if (wave != 0 && sl == 0) {
+        float* q = part[wave - 1][cg];
+        q[0] = st.M;
+        q[1] = st.lw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[2 + c] = st.acc[c];
+    }
+    __syncthreads();
+    if (wave != 0 || sl != 0) return;
+    FoldState w[NW];
+    w[0] = st;
+#pragma unroll
+    for (int k = 1; k < NW; ++k) {
+        const float* q = part[k - 1][cg];
+        w[k].M = q[0];
+        w[k].lw = q[1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[k].acc[c] = q[2 + c];
+    }
+#pragma unroll
+    for (int span = 1; span < NW; span <<= 1)
+#pragma unroll
+        for (int k = 0; k + span < NW; k += 2 * span) w[k] = merge_states(w[k], w[k + span]);
+    st = w[0];
     if (n == 0) {  // nothing visible: defined output +0.0
         *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
         return;
@@ -1261,10 +1294,9 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
         }
         return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
     }
-    // more splits: 32 columns per wave, up to four waves (128 columns) per workgroup
-    const int nw = p.head_dim / 32 < 4 ? p.head_dim / 32 : 4;
-    const dim3 grid(plan->rows * (p.head_dim / (32 * nw)), p.num_kv_heads, p.batch);
-    const dim3 block(64 * nw);
+    // more splits: a workgroup of kCombineWaves waves per 4 combine_cgw(D) columns of a row
+    const dim3 grid(plan->rows * (p.head_dim / (4 * combine_cgw(p.head_dim))), p.num_kv_heads, p.batch);
+    const dim3 block(64 * kCombineWaves);
     switch (p.head_dim) {
         case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, block, 0, s, ca); break;
         case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, block, 0, s, ca); break;

@@ -11,10 +11,9 @@ def pytest_configure(config):
 
 
 def pytest_sessionstart(session):
-    # a fresh checkout has no built library: build it once (hipcc cross-compiles
-    # gfx950 without a GPU); an existing build is used as it is
-    lib = os.path.join(ROOT, "paged_fp8_split_amd", "libpfs.so")
-    if not os.path.exists(lib):
-        from paged_fp8_split_amd import build
+    # build (hipcc cross-compiles gfx950 without a GPU) when a library is
+    # missing or its sources, headers included, changed since it was built
+    from paged_fp8_split_amd import build
 
+    if build.stale():
         build.build()

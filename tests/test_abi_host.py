@@ -284,3 +284,21 @@ def test_codec_host_checks_need_no_device():
     e = _lib.Plan(**dict(BASE, batch=0))
     assert lib.pfs_dequant_paged(e.handle, None, None, None, None, None, None) == 0
     assert lib.pfs_kv_append(e.handle, *([None] * 8), None) == 0
+
+
+def test_build_stamp_tracks_source_content(tmp_path, monkeypatch):
+    """The test session rebuilds libpfs when its sources change: the stamp is
+    a digest of their content (and the headers'), not of file times."""
+    from paged_fp8_split_amd import build
+
+    src = tmp_path / "k.hip"
+    src.write_text("// one\n")
+    d1 = build._digest([str(src)])
+    src.write_text("// two\n")
+    d2 = build._digest([str(src)])
+    assert d1 != d2
+    src.write_text("// one\n")
+    assert build._digest([str(src)]) == d1
+    # a missing stamp or library counts as stale
+    monkeypatch.setattr(build, "LIB", str(tmp_path / "libpfs.so"))
+    assert build.stale()

@@ -55,3 +55,21 @@ def test_noalloc_refuses_a_plan_beyond_its_array():
     with pytest.raises(_lib.PfsError, match="PFS_ERR_WORKSPACE"):
         _lib.verify_noalloc(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
                             t["live_len"], t["q"])
+
+
+def test_package_verify_noalloc_option_matches():
+    """pfs.verify(..., noalloc=True) routes to pfs_verify_noalloc: same
+    bytes as the workspace route; a workspace with it is an error."""
+    w = W.build(seed=304, batch=2, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                lengths=[5000, 1500])
+    t = W.device_tensors(w, device())
+    args = (t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"])
+    kw = dict(head_map=t["head_map"], sm_scale=t["sm_scale"])
+    a = to_np(pfs.verify(*args, **kw))
+    import torch
+
+    out = torch.full_like(t["q"], float("nan"))
+    b = to_np(pfs.verify(*args, **kw, out=out, noalloc=True))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    with pytest.raises(ValueError, match="noalloc"):
+        pfs.verify(*args, **kw, workspace=torch.empty(16, dtype=torch.uint8, device=t["q"].device), noalloc=True)
