@@ -10,16 +10,19 @@ resident in HBM before the timed region starts.
 Timing follows the pages' protocol of graph-replayed operator timing ("[Bugfix]
 Use FP32 state and E4M3 defaults for DFlash2", Test Plan and Results: 20
 warmups, then timed replays): the step (split and combine) is captured once
-as a HIP graph, W untimed warmup replays run, then K timed replays. Before
-every replay an untimed read of a clean 1 GiB buffer evicts the 256 MB
-Infinity Cache and the L2s, so the KV bytes come from HBM. The scrub only
-reads: a scrub that writes leaves dirty lines whose write-back then competes
-with the timed kernel's reads. Each replay is bracketed by HIP events on the
-stream the graph is launched on. `value`, `ms_per_step` and
-`kv_pct_of_peak_hbm` are those replays. The same step launched eagerly (the
-two kernels back to back, events around the step) is reported beside it, and
-a further eager pass with an event between the kernels gives the per-kernel
-figures: the split kernel's mean launch time is the roofline's denominator.
+as a HIP graph; after a 0.3 s pre-warm and W untimed warmup rounds, K timed
+rounds follow. Before every timed run an untimed read of a clean 1 GiB
+buffer evicts the 256 MB Infinity Cache and the L2s, so the KV bytes come
+from HBM. The scrub only reads: a scrub that writes leaves dirty lines whose
+write-back then competes with the timed kernel's reads. Each replay is
+bracketed by HIP events on the stream the graph is launched on. `value`,
+`ms_per_step` and `kv_pct_of_peak_hbm` are those replays. Each round also
+times the same step launched eagerly (the two kernels back to back, events
+around the step) and an eager step with an event between the kernels for
+the per-kernel figures (the split kernel's mean launch time is the
+roofline's denominator); the three alternate in mirrored order round by
+round, as the pages alternate their variants in ABBA blocks, so that all
+three see the same clocks.
 
 Prints one JSON line. `value` is the achieved KV read rate: live K+V bytes of
 the step divided by the mean step time.
@@ -303,31 +306,73 @@ def time_steps(split, combine, evict, stream, steps: int, warmup: int, mid_event
     return split_ms, comb_ms, step_ms, wall
 
 
-def time_graph(graph, evict, stream, steps: int, warmup: int):
-    """Warm up, then time `steps` replays of `graph`, each after an untimed
-    scrub, with HIP events (HipTimer) on `stream` around each replay: the
-    graph's launch is inside the interval. Returns (step_ms, wall_s)."""
+def time_interleaved(graph, split, combine, evict, stream, steps: int, warmup: int, prewarm_s: float = 0.3):
+    """The step three ways, interleaved so that each sees the same GPU state
+    (clock ramp, temperature): as one replay of `graph`, eagerly (split and
+    combine back to back), and eagerly with an event between the kernels
+    (per-kernel times). Each timed run follows an untimed scrub and has HIP
+    events (HipTimer) on `stream` around it; a round runs the three in one
+    order and the next round in the reverse order (A B C, C B A, ...). Before
+    the `warmup` untimed rounds, steps run for `prewarm_s` seconds so that the
+    clocks have ramped up. Returns (graph_ms, eager_ms, split_ms, combine_ms,
+    wall_s) with one entry per timed round."""
     import numpy as np
     import torch
 
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < prewarm_s:
+        evict()
+        graph.replay()
+        evict()
+        split()
+        combine()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         evict()
         graph.replay()
+        evict()
+        split()
+        combine()
     torch.cuda.synchronize()
+    note("warmup done; timing")
     T = timer()
-    evs = [[T.event() for _ in range(2)] for _ in range(steps)]
+    evs = {"g": [[T.event(), T.event()] for _ in range(steps)],
+           "e": [[T.event(), T.event()] for _ in range(steps)],
+           "m": [[T.event(), T.event(), T.event()] for _ in range(steps)]}
+
+    def run_graph(ev):
+        T.record(ev[0], stream)
+        graph.replay()
+        T.record(ev[1], stream)
+
+    def run_eager(ev):
+        T.record(ev[0], stream)
+        split()
+        combine()
+        T.record(ev[1], stream)
+
+    def run_mid(ev):
+        T.record(ev[0], stream)
+        split()
+        T.record(ev[1], stream)
+        combine()
+        T.record(ev[2], stream)
+
+    order = [("g", run_graph), ("e", run_eager), ("m", run_mid)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for k in range(steps):
-        evict()
-        T.record(evs[k][0], stream)
-        graph.replay()
-        T.record(evs[k][1], stream)
+        for key, fn in (order if k % 2 == 0 else order[::-1]):
+            evict()
+            fn(evs[key][k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    res = np.array([T.elapsed_ms(e[0], e[1]) for e in evs])
-    T.destroy([x for e in evs for x in e])
-    return res, wall
+    graph_ms = np.array([T.elapsed_ms(a, b) for a, b in evs["g"]])
+    eager_ms = np.array([T.elapsed_ms(a, b) for a, b in evs["e"]])
+    split_ms = np.array([T.elapsed_ms(e[0], e[1]) for e in evs["m"]])
+    comb_ms = np.array([T.elapsed_ms(e[1], e[2]) for e in evs["m"]])
+    T.destroy([x for v in evs.values() for e in v for x in e])
+    return graph_ms, eager_ms, split_ms, comb_ms, wall
 
 
 def variant(cfg: int, dev, evict, steps: int, warmup: int, kv_format: str = "e4m3",
@@ -616,16 +661,19 @@ def main() -> int:
         _lib.verify(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
                     t["live_len"], out, ws)
     torch.cuda.synchronize()
-    note("graph captured; timing replays")
-    graph_step_ms, wall = time_graph(g, evict, stream, args.steps, args.warmup)
+    g.replay()
+    torch.cuda.synchronize()
     y = out.cpu().numpy()
     out_sha = hashlib.sha256(y.tobytes()).hexdigest()
-    # the same step launched eagerly, kernels back to back
-    _, _, step_ms, _ = time_steps(split, combine, evict, stream, args.steps, 3, mid_event=False)
+    split()
+    combine()
     eager_same = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest() == out_sha
-    # per-kernel figures: an eager pass with an event between the kernels (the
-    # split kernel's launch time is the roofline's denominator)
-    split_ms, comb_ms, _, _ = time_steps(split, combine, evict, stream, args.steps, 0, mid_event=True)
+    note("graph captured; timing replays, eager steps and per-kernel steps, interleaved")
+    # graph replays (the headline), the same step launched eagerly, and an
+    # eager pass with an event between the kernels (the split kernel's launch
+    # time is the roofline's denominator), interleaved round by round
+    graph_step_ms, step_ms, split_ms, comb_ms, wall = time_interleaved(g, split, combine, evict, stream,
+                                                                        args.steps, args.warmup)
 
     # the graph replayed back to back without scrubs (cache-warm: context only)
     T = timer()
@@ -671,7 +719,9 @@ def main() -> int:
         "us_per_step_p10_p50_p90": [round(float(np.percentile(graph_step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "kv_pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "timing": "HIP-graph replay of split + combine, HIP events (hipEventDisableSystemFence) around each replay on "
-                  "its stream (the graph launch inside the interval), Infinity Cache scrubbed before each replay",
+                  "its stream (the graph launch inside the interval), Infinity Cache scrubbed before each replay; "
+                  "replays interleaved round by round (A B C, C B A) with the eager step and the per-kernel pass "
+                  "after a 0.3 s pre-warm",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
