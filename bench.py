@@ -426,7 +426,9 @@ def ceiling(args, dev) -> dict:
     straight into LDS through the split kernel's pipeline of stages; then the
     same number of bytes read from one flat buffer; the split kernel alone
     for comparison. Each launch after the read-only scrub, HIP events
-    (HipTimer) around it; bytes = the live K and V bytes."""
+    (HipTimer) around it; bytes = the live K and V bytes. Then the combine
+    against a flat read of the same partial bytes, each straight after a
+    split (its floor for one burst of reads of that size)."""
     import ctypes
 
     import numpy as np
@@ -496,6 +498,39 @@ def ceiling(args, dev) -> dict:
         res[name] = {"us_mean": round(float(ms.mean()) * 1e3, 2), "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
                      "kv_TBps": round(kv / (float(ms.mean()) * 1e-3) / 1e12, 3),
                      "frac_of_8TBps": round(kv / (float(ms.mean()) * 1e-3) / 1e12 / 8.0, 4)}
+
+    # the combine's floor: the workspace's partial bytes read flat (register
+    # loads, 512 workgroups) straight after a split, as the combine reads them,
+    # against the combine itself; each after an untimed scrub and split
+    out = torch.empty_like(t["q"])
+    part_bytes = (plan.workspace_bytes // 16) * 16
+    part_grid = 512
+    psink = torch.empty(part_grid * 512, dtype=torch.int32, device=dev)
+
+    def combine():
+        _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws, stream)
+
+    def partials_read():
+        assert lib.pfs_probe_flat(ws.data_ptr(), part_bytes, part_grid, psink.data_ptr(), sp) == 0
+
+    ccases = {"combine": combine, "partials_flat_read": partials_read}
+    ctimes = {k: [] for k in ccases}
+    for r in range(args.steps):
+        for name, fn in ccases.items():
+            torch.sum(scrub, 0, out=scrub_sink)
+            split()
+            e0, e1 = T.event(), T.event()
+            T.record(e0, stream)
+            fn()
+            T.record(e1, stream)
+            ctimes[name].append(T.elapsed_ms(e0, e1))
+            T.destroy([e0, e1])
+    res["combine_floor"] = {"partial_bytes": part_bytes, "flat_read_workgroups": part_grid}
+    for name, ms in ctimes.items():
+        ms = np.array(ms)
+        res["combine_floor"][name] = {"us_mean": round(float(ms.mean()) * 1e3, 2),
+                                      "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                                      "TBps": round(part_bytes / (float(ms.mean()) * 1e-3) / 1e12, 3)}
     return res
 
 
