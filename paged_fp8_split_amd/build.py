@@ -54,7 +54,10 @@ def _digest(sources) -> str:
     inc = os.path.join(os.path.dirname(HERE), "include")
     headers = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h"))
     headers += sorted(os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h"))
-    h = hashlib.sha256(" ".join(flags()).encode())
+    # the include root is this tree's own path: hashed as a placeholder, so a
+    # copy of the tree elsewhere keeps its build current
+    root = os.path.dirname(HERE)
+    h = hashlib.sha256(" ".join("<root>" if f == root else f for f in flags()).encode())
     for path in list(sources) + headers:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())

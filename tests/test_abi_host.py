@@ -302,3 +302,20 @@ def test_build_stamp_tracks_source_content(tmp_path, monkeypatch):
     # a missing stamp or library counts as stale
     monkeypatch.setattr(build, "LIB", str(tmp_path / "libpfs.so"))
     assert build.stale()
+
+
+def test_build_stamp_does_not_depend_on_the_tree_path(tmp_path, monkeypatch):
+    """A copy of the tree elsewhere (as on another machine) keeps its build
+    current: the digest hashes the include root as a placeholder."""
+    import shutil
+
+    from paged_fp8_split_amd import build
+
+    ref = build._digest(build.SOURCES)
+    pkg = tmp_path / "paged_fp8_split_amd"
+    shutil.copytree(build.CSRC, pkg / "csrc")
+    shutil.copytree(os.path.join(os.path.dirname(build.HERE), "include"), tmp_path / "include")
+    monkeypatch.setattr(build, "HERE", str(pkg))
+    monkeypatch.setattr(build, "CSRC", str(pkg / "csrc"))
+    moved = [str(pkg / "csrc" / os.path.basename(s)) for s in build.SOURCES]
+    assert build._digest(moved) == ref
