@@ -140,14 +140,20 @@ __device__ __forceinline__ uint32_t residual_f16x2(float p0, float p1, uint32_t 
     return r;
 }
 
+// Maximum of two scores that are never NaN (finite or -inf): the median of
+// (a, b, +inf), one v_med3_f32, where fmaxf would first quiet both inputs
+// (a v_max_f32 x, x each). pinf holds +inf in a register the compiler does
+// not see through, so that it keeps the median.
+__device__ __forceinline__ float max_no_nan(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+
 // Max over the four lanes l, l^16, l^32, l^48 (the lane groups holding one
 // result column). v_permlane16/32_swap return both halves of a swap; the max
 // of the pair is the xor-16 / xor-32 butterfly step, identical in every lane.
-__device__ __forceinline__ float max_over_lane_groups(float v) {
+__device__ __forceinline__ float max_over_lane_groups(float v, float pinf) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = max_no_nan(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
     auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    return max_no_nan(__uint_as_float(c[0]), __uint_as_float(c[1]), pinf);
 }
 
 __device__ __forceinline__ int32_t clamp_i(int64_t v, int64_t lo, int64_t hi) {
@@ -392,6 +398,9 @@ pfs_split_kernel(const SplitArgs a) {
     // block-table entry together without also waiting for the Q reads below.
     int vzero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    // +inf for max_no_nan
+    float pinf;
+    asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
     const int32_t L_raw = a.live_len[b + vzero];
     const float kscale_g = a.kscale[g];
     // ---- Q^T operands in registers: (nt, ks) holds row r_wave + 16 nt + lc,
@@ -643,9 +652,10 @@ pfs_split_kernel(const SplitArgs a) {
         }
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) {
-            const float mx = fmaxf(fmaxf(fmaxf(xs[nt][0], xs[nt][1]), fmaxf(xs[nt][2], xs[nt][3])),
-                                   fmaxf(fmaxf(xs[nt][4], xs[nt][5]), fmaxf(xs[nt][6], xs[nt][7])));
-            smax[nt] = max_over_lane_groups(mx);
+            const float m01 = max_no_nan(xs[nt][0], xs[nt][1], pinf), m23 = max_no_nan(xs[nt][2], xs[nt][3], pinf);
+            const float m45 = max_no_nan(xs[nt][4], xs[nt][5], pinf), m67 = max_no_nan(xs[nt][6], xs[nt][7], pinf);
+            const float mx = max_no_nan(max_no_nan(m01, m23, pinf), max_no_nan(m45, m67, pinf), pinf);
+            smax[nt] = max_over_lane_groups(mx, pinf);
             if (!edge) smax[nt] *= cscale;
             need |= (smax[nt] > mref[nt] + kTau);
         }
