@@ -116,6 +116,20 @@ def split_algorithmic_bytes(w, plan) -> int:
     return kv + qb + bt + ws
 
 
+def step_algorithmic_bytes(w, plan) -> int:
+    """Bytes one verify step must move: the split kernel's (live K+V, Q,
+    block-table entries, FP32 partials written), the combine's read of those
+    partials, and the FP16 output."""
+    import numpy as np
+
+    L = np.clip(w.live_len.astype(np.int64), 0, w.capacity)
+    rows = w.q * w.group
+    splits = int((-(-L // plan.tokens_per_split)).sum())
+    ws = splits * w.num_kv_heads * rows * (w.head_dim + 2) * 4
+    out = w.batch * w.q * w.num_q_heads * w.head_dim * 2
+    return split_algorithmic_bytes(w, plan) + ws + out
+
+
 def mfma_report(w, split_ms: float, cfg) -> dict:
     """Matrix-core use of the split kernel: the dense FP16 work over the mean
     launch time against the FP16 MFMA peak, and the MFMA-busy fraction that
@@ -738,6 +752,7 @@ def main() -> int:
     eager_ms = float(step_ms.mean())
     value = kv / (mean_ms * 1e-3) / 1e9
     split_bytes = split_algorithmic_bytes(w, plan)
+    step_bytes = step_algorithmic_bytes(w, plan)
     split_mean_ms = float(split_ms.mean())
     achieved = split_bytes / (split_mean_ms * 1e-3) / 1e9
     default_line = args.pv_mode == "high_residual" and args.kv_format == "e4m3" and args.tokens_per_split == 0
@@ -753,6 +768,10 @@ def main() -> int:
         "us_per_step": round(mean_ms * 1e3, 2),
         "us_per_step_p10_p50_p90": [round(float(np.percentile(graph_step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "kv_pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        # every byte the step must move (the split kernel's, plus the combine's
+        # read of the partials and its FP16 output) over the same replay time
+        "step_algorithmic_bytes": step_bytes,
+        "step_algorithmic_GBps": round(step_bytes / (mean_ms * 1e-3) / 1e9, 2),
         "timing": "HIP-graph replay of split + combine, HIP events (hipEventDisableSystemFence) around each replay on "
                   "its stream (the graph launch inside the interval), Infinity Cache scrubbed before each replay; "
                   "replays interleaved round by round (A B C, C B A) with the eager step and the per-kernel pass "
