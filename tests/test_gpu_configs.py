@@ -157,3 +157,31 @@ def test_graph_replay_with_changed_lengths_and_pages():
         ye = to_np(run(wk, tensors=t)[0])
         assert np.array_equal(yg.view(np.uint16), ye.view(np.uint16)), f"case {k}"
         judge(yg, oracle_ref(wk), f"replay lengths {lens}")
+
+
+@pytest.mark.parametrize("cus", [40, 80, 304])
+def test_plans_for_other_compute_unit_counts(cus):
+    """The default split length fills the CU count the plan is given (a
+    CU-masked or partitioned device passes its own): other counts give other
+    split lengths, and every one of them matches the oracle."""
+    import torch
+
+    w = W.build(seed=610, batch=1, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                lengths=[40000], outlier_frac=0.01)
+    dev = device()
+    t = W.device_tensors(w, dev)
+    plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"],
+                         k_pool=t["k_pool"], max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"],
+                         num_cus=cus)
+    assert plan.num_cus == cus
+    # one round of split workgroups over the given CUs, with the shortest
+    # such split (a multiple of 64 tokens, at least 256)
+    cap, tps = w.max_pages_per_row * w.page_size, plan.tokens_per_split
+    assert plan.num_splits * w.num_kv_heads <= cus
+    assert tps == 256 or -(-cap // (tps - 64)) * w.num_kv_heads > cus
+    out = torch.empty_like(t["q"])
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
+               head_map=t["head_map"], sm_scale=t["sm_scale"], out=out, workspace=ws, plan=plan)
+    log(f"[num_cus {cus}] {plan.num_splits} splits x {plan.tokens_per_split} tokens")
+    judge(to_np(out), oracle_ref(w), f"num_cus {cus}")
