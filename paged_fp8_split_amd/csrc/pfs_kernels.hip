@@ -9,8 +9,12 @@
 //   pfs_split_kernel      per-split QK^T (MFMA), online softmax, PV (MFMA);
 //                         emits FP32 (max, sum, unnormalized PV) per split
 //   pfs_combine_kernel    rescales the splits, sums them in a fixed order
-//                         (ascending within a split lane, lanes in order),
-//                         normalizes and rounds once to FP16
+//                         (ascending within contiguous split blocks, then a
+//                         fixed pairwise tree over the blocks: wavefront
+//                         shuffles, then LDS across waves), normalizes and
+//                         rounds once to FP16
+//   pfs_combine_rows_kernel  the same for plans with at most 32 splits, each
+//                         thread summing its row's splits in ascending order
 //
 // The method ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32
 // partials", final status, revision 3 bullet; "[Kernel] Finalize the audited
