@@ -71,6 +71,62 @@ def _pool_layout(pool):
     return int(pages), int(page), int(hkv), int(d), tuple(int(s) for s in pool.stride()[:3])
 
 
+# The kernels address every buffer from the plan's sizes alone, so the
+# binding checks each tensor against them before a pointer crosses the ABI:
+# a short block table, length vector, scale vector or output would otherwise
+# be read or written past its end on the device.
+
+def _require(ok: bool, msg: str) -> None:
+    if not ok:
+        raise ValueError(msg)
+
+
+def _check_pools(k_pool, v_pool) -> None:
+    _require(k_pool.stride() == v_pool.stride() and k_pool.shape == v_pool.shape,
+             "K and V pools must share shape and strides")
+    _require(v_pool.dtype == k_pool.dtype, "K and V pools must share a dtype")
+
+
+def _check_request_tensors(batch: int, hkv: int, block_table, live_len, scales) -> None:
+    """block_table [batch, pages per row] int32, live_len [batch] int32 and
+    each named scale [hkv] float32, all contiguous."""
+    import torch
+
+    _require(block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.dim() == 2
+             and int(block_table.shape[0]) == batch,
+             f"block_table must be a contiguous int32 tensor [{batch}, max_pages_per_row]")
+    _require(live_len.dtype == torch.int32 and live_len.is_contiguous() and live_len.numel() == batch,
+             f"live_len must be a contiguous int32 tensor of {batch} lengths")
+    for name, t in scales:
+        _require(t.dtype == torch.float32 and t.is_contiguous() and t.numel() == hkv,
+                 f"{name} must be a contiguous float32 tensor [{hkv}]")
+
+
+def _check_out(out, shape) -> None:
+    import torch
+
+    _require(out.dtype == torch.float16 and out.is_contiguous() and tuple(out.shape) == tuple(shape),
+             f"out must be a contiguous float16 tensor {list(shape)}")
+
+
+def _check_device(tensors) -> None:
+    """Every tensor on one GPU (checked last, so that a host-only caller
+    sees the other errors first and no host pointer reaches the library)."""
+    dev = tensors[0][1].device
+    for name, t in tensors:
+        _require(t.is_cuda and t.device == dev, f"{name} must be on the GPU that holds {tensors[0][0]} ({dev})")
+
+
+def _check_plan(plan, *, batch, q, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_row,
+                num_pool_pages, strides) -> None:
+    p = plan.problem
+    got = (p.batch, p.q, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.max_pages_per_row,
+           p.num_pool_pages, (p.kv_page_stride, p.kv_token_stride, p.kv_head_stride))
+    want = (batch, q, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_row, num_pool_pages,
+            tuple(strides))
+    _require(got == want, f"the plan was made for another shape: {got} against the tensors' {want}")
+
+
 def make_plan(*, batch, q, num_q_heads, head_map, k_pool, max_pages_per_row, sm_scale=None,
               partition_tokens=64, tokens_per_split=0, kv_format: Optional[str] = None,
               pv_mode: str = "high_residual", num_cus: Optional[int] = None):
@@ -119,6 +175,9 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     block_table  [B, max_pages_per_row] int32
     live_len     [B] int32, draft tokens included
     head_map     query head -> KV head (default h // (Hq // Hkv))
+    plan         a plan from ``make_plan`` for exactly these shapes and pool
+                 layout (checked); its head map, scale, split length and
+                 probability mode then apply
     noalloc      keep the split partials in the library's per-GPU device
                  array (pfs_verify_noalloc) instead of a workspace; with
                  ``out`` given, nothing is allocated. Calls that overlap on
@@ -128,12 +187,17 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
     from . import _lib
     import torch
 
+    _require(q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 4,
+             "q must be a contiguous float16 tensor [B, q, Hq, D]")
     B, nq, Hq, D = (int(x) for x in q.shape)
-    if q.dtype != torch.float16 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous float16 tensor [B, q, Hq, D]")
-    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
-        raise ValueError("K and V pools must share shape and strides")
-    hkv = int(k_pool.shape[2])
+    _check_pools(k_pool, v_pool)
+    pages, page, hkv, d, strides = _pool_layout(k_pool)
+    _require(d == D, f"q has head_dim {D}, the pools {d}")
+    _check_request_tensors(B, hkv, block_table, live_len, (("k_scale", k_scale), ("v_scale", v_scale)))
+    if out is not None:
+        _check_out(out, q.shape)
+    if workspace is not None:
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
     if head_map is None:
         head_map = [h // (Hq // hkv) for h in range(Hq)] if Hq % hkv == 0 else list(range(Hq))
     if plan is None:
@@ -141,14 +205,14 @@ def verify(q, k_pool, v_pool, k_scale, v_scale, block_table, live_len, *, head_m
                          max_pages_per_row=int(block_table.shape[1]), sm_scale=sm_scale,
                          partition_tokens=partition_tokens, tokens_per_split=tokens_per_split,
                          kv_format=kv_format, pv_mode=pv_mode)
-    elif plan.kv_format != _kv_format(k_pool, kv_format):
-        raise ValueError("the plan's KV format differs from the pools'")
-    if v_pool.dtype != k_pool.dtype:
-        raise ValueError("K and V pools must share a dtype")
-    for name, t, dt in (("k_scale", k_scale, torch.float32), ("v_scale", v_scale, torch.float32),
-                        ("block_table", block_table, torch.int32), ("live_len", live_len, torch.int32)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    else:
+        _check_plan(plan, batch=B, q=nq, num_q_heads=Hq, num_kv_heads=hkv, head_dim=D, page_size=page,
+                    max_pages_per_row=int(block_table.shape[1]), num_pool_pages=pages, strides=strides)
+        _require(plan.kv_format == _kv_format(k_pool, kv_format), "the plan's KV format differs from the pools'")
+    named = [("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_scale", k_scale), ("v_scale", v_scale),
+             ("block_table", block_table), ("live_len", live_len)]
+    named += [(n, t) for n, t in (("out", out), ("workspace", workspace)) if t is not None]
+    _check_device(named)
     if out is None:
         out = torch.empty_like(q)
     if noalloc:
@@ -172,13 +236,19 @@ def dequant_paged(pool, block_table, live_len, *, scale=None, out=None, stream=N
     import torch
 
     pages, page, hkv, d, _ = _pool_layout(pool)
+    _require(block_table.dim() == 2, "block_table must be a 2-D int32 tensor [B, max_pages_per_row]")
     B = int(block_table.shape[0])
-    if scale is not None and (scale.dtype != torch.float32 or not scale.is_contiguous() or scale.numel() != hkv):
-        raise ValueError("scale must be a contiguous float32 tensor [num_kv_heads]")
+    _check_request_tensors(B, hkv, block_table, live_len, () if scale is None else (("scale", scale),))
+    shape = (B, int(block_table.shape[1]) * page, hkv, d)
+    if out is not None:
+        _check_out(out, shape)
+    named = [("pool", pool), ("block_table", block_table), ("live_len", live_len)]
+    named += [(n, t) for n, t in (("scale", scale), ("out", out)) if t is not None]
+    _check_device(named)
     plan = make_plan(batch=B, q=1, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=pool,
                      max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0, kv_format=kv_format)
     if out is None:
-        out = torch.empty((B, plan.capacity, hkv, d), dtype=torch.float16, device=pool.device)
+        out = torch.empty(shape, dtype=torch.float16, device=pool.device)
     _lib.dequant_paged(plan, pool, block_table, live_len, out, stream, scale=scale)
     return out
 
@@ -193,17 +263,17 @@ def kv_append(k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_p
     from . import _lib
     import torch
 
+    _require(k_new.dim() == 4, "k_new must be a contiguous float16 tensor [B, q, Hkv, D]")
     B, nq, hkv, d = (int(x) for x in k_new.shape)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
-        if t.dtype != torch.float16 or not t.is_contiguous() or tuple(t.shape) != (B, nq, hkv, d):
-            raise ValueError(f"{name} must be a contiguous float16 tensor [B, q, Hkv, D]")
-    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
-        raise ValueError("K and V pools must share shape and strides")
+        _require(t.dtype == torch.float16 and t.is_contiguous() and tuple(t.shape) == (B, nq, hkv, d),
+                 f"{name} must be a contiguous float16 tensor [B, q, Hkv, D]")
+    _check_pools(k_pool, v_pool)
     pages, page, phkv, pd, _ = _pool_layout(k_pool)
-    if (phkv, pd) != (hkv, d):
-        raise ValueError("k_new and the pools disagree on num_kv_heads / head_dim")
-    if v_pool.dtype != k_pool.dtype:
-        raise ValueError("K and V pools must share a dtype")
+    _require((phkv, pd) == (hkv, d), "k_new and the pools disagree on num_kv_heads / head_dim")
+    _check_request_tensors(B, hkv, block_table, live_len, (("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_device([("k_new", k_new), ("v_new", v_new), ("k_scale", k_scale), ("v_scale", v_scale),
+                   ("block_table", block_table), ("live_len", live_len), ("k_pool", k_pool), ("v_pool", v_pool)])
     plan = make_plan(batch=B, q=nq, num_q_heads=hkv, head_map=list(range(hkv)), k_pool=k_pool,
                      max_pages_per_row=int(block_table.shape[1]), sm_scale=1.0, kv_format=kv_format)
     _lib.kv_append(plan, k_new, v_new, k_scale, v_scale, block_table, live_len, k_pool, v_pool, stream)

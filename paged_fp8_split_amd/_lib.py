@@ -146,6 +146,7 @@ class Plan:
                                   int(kv_page_stride),
                                   int(kv_token_stride), int(kv_head_stride), float(sm_scale),
                                   ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32)))
+        self._head_map = hm  # the problem struct points at it
         handle = ctypes.c_void_p()
         st = lib.pfs_plan_create(ctypes.byref(self.problem), ctypes.byref(handle))
         if st != 0:

@@ -319,3 +319,83 @@ def test_build_stamp_does_not_depend_on_the_tree_path(tmp_path, monkeypatch):
     monkeypatch.setattr(build, "CSRC", str(pkg / "csrc"))
     moved = [str(pkg / "csrc" / os.path.basename(s)) for s in build.SOURCES]
     assert build._digest(moved) == ref
+
+
+def _host_problem():
+    import torch
+
+    B, nq, Hq, Hkv, D, page, pages, mppr = 2, 4, 4, 1, 64, 16, 8, 4
+    return dict(q=torch.zeros(B, nq, Hq, D, dtype=torch.float16),
+                k_pool=torch.zeros(pages, page, Hkv, D, dtype=torch.uint8),
+                v_pool=torch.zeros(pages, page, Hkv, D, dtype=torch.uint8),
+                k_scale=torch.ones(Hkv), v_scale=torch.ones(Hkv),
+                block_table=torch.zeros(B, mppr, dtype=torch.int32), live_len=torch.zeros(B, dtype=torch.int32))
+
+
+def test_package_verify_checks_every_tensor_before_the_library():
+    """The kernels size every buffer from the plan, so the binding refuses a
+    tensor that does not match it (a short block table, length or scale
+    vector, a wrong output, a plan made for other shapes), and tensors that
+    are not on the GPU, before any pointer reaches the library."""
+    import torch
+
+    import paged_fp8_split_amd as pfs
+
+    a = _host_problem()
+    q, bt, ll, ks = a["q"], a["block_table"], a["live_len"], a["k_scale"]
+    bad = [
+        dict(q=q.float()),
+        dict(q=q[:, :, :, :32]),
+        dict(q=torch.zeros(2, 4, 4, 128, dtype=torch.float16)),
+        dict(v_pool=a["v_pool"][:4]),
+        dict(v_pool=a["v_pool"].view(torch.float8_e5m2)),
+        dict(block_table=bt[:1]),
+        dict(block_table=bt.to(torch.int64)),
+        dict(block_table=bt.reshape(-1)),
+        dict(live_len=ll[:1]),
+        dict(live_len=ll.to(torch.int64)),
+        dict(k_scale=torch.ones(2)),
+        dict(v_scale=ks.double()),
+        dict(out=torch.zeros(1, 4, 4, 64, dtype=torch.float16)),
+        dict(out=torch.zeros(2, 4, 4, 64, dtype=torch.float32)),
+    ]
+    for over in bad:
+        with pytest.raises(ValueError) as e:
+            pfs.verify(**{**a, **over})
+        assert "GPU" not in str(e.value), over  # refused by its own check, not the device check
+    other = pfs.make_plan(batch=1, q=4, num_q_heads=4, head_map=[0] * 4, k_pool=a["k_pool"], max_pages_per_row=4)
+    with pytest.raises(ValueError, match="another shape"):
+        pfs.verify(**a, plan=other)
+    # every shape consistent, but host tensors: refused by the binding
+    with pytest.raises(ValueError, match="GPU"):
+        pfs.verify(**a)
+    with pytest.raises(ValueError, match="GPU"):
+        pfs.verify(**a, noalloc=True, out=torch.zeros_like(q))
+
+
+def test_package_codec_calls_check_every_tensor_before_the_library():
+    import torch
+
+    import paged_fp8_split_amd as pfs
+
+    a = _host_problem()
+    kp, vp, bt, ll, ks, vs = (a[k] for k in ("k_pool", "v_pool", "block_table", "live_len", "k_scale", "v_scale"))
+    for over in (dict(block_table=bt[:, :2].contiguous().to(torch.int64)), dict(live_len=ll[:1]),
+                 dict(scale=torch.ones(3)), dict(out=torch.zeros(2, 32, 1, 64, dtype=torch.float16))):
+        args = dict(block_table=bt, live_len=ll)
+        args.update(over)
+        with pytest.raises(ValueError) as e:
+            pfs.dequant_paged(kp, **args)
+        assert "GPU" not in str(e.value), over
+    with pytest.raises(ValueError, match="GPU"):
+        pfs.dequant_paged(kp, bt, ll, scale=ks, out=torch.zeros(2, 64, 1, 64, dtype=torch.float16))
+    kn = torch.zeros(2, 4, 1, 64, dtype=torch.float16)
+    for over in (dict(v_new=kn[:1]), dict(block_table=bt[:1]), dict(live_len=ll.to(torch.int64)),
+                 dict(v_scale=torch.ones(2)), dict(v_pool=vp[:, :8]), dict(k_new=kn.reshape(2, 4, 64))):
+        args = dict(k_new=kn, v_new=kn, k_scale=ks, v_scale=vs, block_table=bt, live_len=ll, k_pool=kp, v_pool=vp)
+        args.update(over)
+        with pytest.raises(ValueError) as e:
+            pfs.kv_append(**args)
+        assert "GPU" not in str(e.value), over
+    with pytest.raises(ValueError, match="GPU"):
+        pfs.kv_append(kn, kn, ks, vs, bt, ll, kp, vp)
