@@ -15,6 +15,9 @@
 //                         rounds once to FP16
 //   pfs_combine_rows_kernel  the same for plans with at most 32 splits, each
 //                         thread summing its row's splits in ascending order
+//                         (both read only the splits that hold visible keys;
+//                         a single request issues its first reads before its
+//                         live length is known)
 //
 // The method ("[Kernel][SM70] Add opt-in E4M3 grouped attention with FP32
 // partials", final status, revision 3 bullet; "[Kernel] Finalize the audited
@@ -981,15 +984,16 @@ __device__ __forceinline__ void fold_splits(FoldState& st, const float2 (&v)[N],
 }
 
 // Loads the partials of N consecutive splits s0, s0 + 1, ... of one row
-// (slot0 + s * stride), at indices clamped to the plan's last split so that
-// no load sits under a branch; the caller selects the valid ones.
+// (slot0 + s * stride), at indices clamped to split s_last so that no load
+// sits under a branch; the caller selects the valid ones. Clamped loads
+// repeat an address already being read and fetch nothing more from HBM.
 template <int N>
-__device__ __forceinline__ void load_splits(const CombineArgs& a, int64_t slot0, int64_t stride, int s0, int col0,
-                                            float2 (&v)[N], f32x4 (&x)[N]) {
+__device__ __forceinline__ void load_splits(const CombineArgs& a, int64_t slot0, int64_t stride, int s0, int s_last,
+                                            int col0, float2 (&v)[N], f32x4 (&x)[N]) {
     const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-        const int64_t slot = slot0 + (int64_t)min(s0 + u, a.num_splits - 1) * stride;
+        const int64_t slot = slot0 + (int64_t)min(s0 + u, s_last) * stride;
         v[u] = ml[slot];
         x[u] = *reinterpret_cast<const f32x4*>(a.ws_acc + slot * a.head_dim + col0);
     }
@@ -1041,7 +1045,7 @@ __device__ __forceinline__ FoldState merge_states(const FoldState& l, const Fold
     return o;
 }
 
-template <int D>
+template <int D, bool AHEAD>
 __global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const CombineArgs a) {
     constexpr int CGW = combine_cgw(D);  // 4-column groups per wave
     constexpr int SL = 64 / CGW;         // split blocks per wave
@@ -1066,19 +1070,26 @@ __global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const C
     const int s_begin = (wave * SL + sl) * C;
     const int s_end = min(s_begin + C, a.num_splits);
 
+    // AHEAD (one request): the first round of loads goes out before the live
+    // length arrives (its splits are normally all visible). A batch's lengths
+    // vary, so there the loads wait for it and stop at the last visible split.
     const int32_t L_raw = a.live_len[b];
     float2 v[R];
     f32x4 x[R];
-    load_splits<R>(a, slot0, stride, s_begin, col0, v, x);
+    if constexpr (AHEAD) load_splits<R>(a, slot0, stride, s_begin, a.num_splits - 1, col0, v, x);
     const int32_t L = clamp_i(L_raw, 0, a.capacity);
     const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
     const int ns = (n + a.tokens_per_split - 1) / a.tokens_per_split;  // splits holding visible keys
     const int s_lim = min(s_end, ns);
+    // clamped loads repeat a visible split (or split 0); with AHEAD the loads
+    // of the first round could not know the live length, nor do the others
+    const int s_last = AHEAD ? a.num_splits - 1 : max(ns - 1, 0);
+    if constexpr (!AHEAD) load_splits<R>(a, slot0, stride, s_begin, s_last, col0, v, x);
     FoldState st{-INFINITY, 0.0f, f32x4{0.f, 0.f, 0.f, 0.f}};
     select_splits<R>(s_begin, s_lim, v, x);
     fold_splits<R>(st, v, x);
     for (int s0 = s_begin + R; s0 < s_lim; s0 += R) {
-        load_splits<R>(a, slot0, stride, s0, col0, v, x);
+        load_splits<R>(a, slot0, stride, s0, s_last, col0, v, x);
         select_splits<R>(s0, s_lim, v, x);
         fold_splits<R>(st, v, x);
     }
@@ -1131,7 +1142,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void pfs_combine_kernel(const C
 // folds every visible split of that row itself, in ascending order, 8 at a
 // time (the first 8 loads issued before the live length has arrived), with
 // no cross-lane merge; a workgroup covers 1024 / D whole rows.
-template <int D>
+template <int D, bool AHEAD>
 __global__ __launch_bounds__(256) void pfs_combine_rows_kernel(const CombineArgs a) {
     constexpr int R = 8;
     constexpr int TPR = D / 4;        // threads per row
@@ -1148,10 +1159,12 @@ __global__ __launch_bounds__(256) void pfs_combine_rows_kernel(const CombineArgs
     const int64_t stride = (int64_t)a.batch * a.num_kv_heads * a.rows;
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + g) * a.rows + r;
 
+    // (the first round ahead of the live length with AHEAD, as in
+    // pfs_combine_kernel)
     const int32_t L_raw = a.live_len[b];
     float2 v[R];
     f32x4 x[R];
-    load_splits<R>(a, slot0, stride, 0, col0, v, x);
+    if constexpr (AHEAD) load_splits<R>(a, slot0, stride, 0, a.num_splits - 1, col0, v, x);
     const int32_t L = clamp_i(L_raw, 0, a.capacity);
     const int32_t n = clamp_i((int64_t)L - a.q + i + 1, 0, L);
     if (n == 0) {
@@ -1159,11 +1172,13 @@ __global__ __launch_bounds__(256) void pfs_combine_rows_kernel(const CombineArgs
         return;
     }
     const int ns = min((n + a.tokens_per_split - 1) / a.tokens_per_split, a.num_splits);
+    if constexpr (!AHEAD) load_splits<R>(a, slot0, stride, 0, ns - 1, col0, v, x);
+    const int s_last = AHEAD ? a.num_splits - 1 : ns - 1;
     FoldState st{-INFINITY, 0.0f, f32x4{0.f, 0.f, 0.f, 0.f}};
     select_splits<R>(0, ns, v, x);
     fold_splits<R>(st, v, x);
     for (int s0 = R; s0 < ns; s0 += R) {
-        load_splits<R>(a, slot0, stride, s0, col0, v, x);
+        load_splits<R>(a, slot0, stride, s0, s_last, col0, v, x);
         select_splits<R>(s0, ns, v, x);
         fold_splits<R>(st, v, x);
     }
@@ -1277,6 +1292,29 @@ int32_t pfs_launch_split(const pfs_plan* plan, const void* q, const uint8_t* k_p
     return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
 
+// Plans with at most kCombineRowSplits splits: one thread per 4 columns of a
+// row folds every split of it (pfs_combine_rows_kernel); more splits: a
+// workgroup of kCombineWaves waves per 4 combine_cgw(D) columns of a row.
+// One request issues its first partial loads ahead of its live length.
+template <int D>
+hipError_t launch_combine(const pfs_plan& plan, const CombineArgs& ca, bool ahead, hipStream_t s) {
+    const pfs_problem& p = plan.p;
+    if (plan.num_splits <= kCombineRowSplits) {
+        const dim3 grid((plan.rows * D / 4 + 255) / 256, p.num_kv_heads, p.batch);
+        if (ahead)
+            hipLaunchKernelGGL((pfs_combine_rows_kernel<D, true>), grid, dim3(256), 0, s, ca);
+        else
+            hipLaunchKernelGGL((pfs_combine_rows_kernel<D, false>), grid, dim3(256), 0, s, ca);
+    } else {
+        const dim3 grid(plan.rows * (D / (4 * combine_cgw(D))), p.num_kv_heads, p.batch);
+        if (ahead)
+            hipLaunchKernelGGL((pfs_combine_kernel<D, true>), grid, dim3(64 * kCombineWaves), 0, s, ca);
+        else
+            hipLaunchKernelGGL((pfs_combine_kernel<D, false>), grid, dim3(64 * kCombineWaves), 0, s, ca);
+    }
+    return hipGetLastError();
+}
+
 int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int32_t* live_len, void* out,
                            const void* workspace, pfs_stream_t stream) {
     const pfs_problem& p = plan->p;
@@ -1298,24 +1336,13 @@ int32_t pfs_launch_combine(const pfs_plan* plan, const float* v_scale, const int
     ca.head_dim = p.head_dim;
     for (int i = 0; i < pfs::kMaxQHeads; ++i) ca.qhead[i] = plan->qhead[i];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (plan->num_splits <= kCombineRowSplits) {  // each thread folds every split of its row
-        const dim3 rgrid((plan->rows * p.head_dim / 4 + 255) / 256, p.num_kv_heads, p.batch);
-        switch (p.head_dim) {
-            case 64: hipLaunchKernelGGL(pfs_combine_rows_kernel<64>, rgrid, dim3(256), 0, s, ca); break;
-            case 128: hipLaunchKernelGGL(pfs_combine_rows_kernel<128>, rgrid, dim3(256), 0, s, ca); break;
-            case 256: hipLaunchKernelGGL(pfs_combine_rows_kernel<256>, rgrid, dim3(256), 0, s, ca); break;
-            default: return PFS_ERR_UNSUPPORTED;
-        }
-        return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
-    }
-    // more splits: a workgroup of kCombineWaves waves per 4 combine_cgw(D) columns of a row
-    const dim3 grid(plan->rows * (p.head_dim / (4 * combine_cgw(p.head_dim))), p.num_kv_heads, p.batch);
-    const dim3 block(64 * kCombineWaves);
+    const bool ahead = p.batch == 1;
+    hipError_t e;
     switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL(pfs_combine_kernel<64>, grid, block, 0, s, ca); break;
-        case 128: hipLaunchKernelGGL(pfs_combine_kernel<128>, grid, block, 0, s, ca); break;
-        case 256: hipLaunchKernelGGL(pfs_combine_kernel<256>, grid, block, 0, s, ca); break;
+        case 64: e = launch_combine<64>(*plan, ca, ahead, s); break;
+        case 128: e = launch_combine<128>(*plan, ca, ahead, s); break;
+        case 256: e = launch_combine<256>(*plan, ca, ahead, s); break;
         default: return PFS_ERR_UNSUPPORTED;
     }
-    return hipGetLastError() == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
+    return e == hipSuccess ? PFS_OK : PFS_ERR_LAUNCH;
 }
