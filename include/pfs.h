@@ -253,7 +253,8 @@ int32_t pfs_verify_combine(const pfs_plan* plan, const float* v_scale, const int
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. The split partials live in a device
  * array inside the library instead (one per GPU, pfs_noalloc_scratch_bytes()
- * = 128 MiB, held from the first call on that GPU until the process ends);
+ * = 128 MiB, held from the first call on that GPU until the process ends;
+ * the call uses the array of the GPU that runs `stream`);
  * the kernels, the arithmetic and therefore the output bits are those of
  * pfs_verify with the same plan. The call allocates nothing: no hipMalloc,
  * hipFree or allocating library routine (its first call on a device looks

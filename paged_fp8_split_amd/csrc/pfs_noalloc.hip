@@ -5,8 +5,9 @@
 // kernels are the ones pfs_verify launches.
 //
 // Each GPU the library runs on holds its own copy of the array (module
-// memory, kept until the process ends). Its device address is taken once per
-// device with hipGetSymbolAddress while that device is current; host code
+// memory, kept until the process ends). The call uses the copy of the GPU
+// that runs its stream; that copy's device address is taken once per device
+// with hipGetSymbolAddress while that device is current; host code
 // only ever passes that address, never the array's name (on the host the name
 // is a stand-in, not a device address). The verify workspace needs no
 // initialization (every partial the combine reads is written earlier in the
@@ -29,10 +30,14 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];
 std::mutex g_scratch_mutex;
 
-// Device address of the current device's copy of `scratch` (nullptr on error).
-void* device_scratch(int* status) {
+// Device address of the copy of `scratch` on the GPU that runs `stream` (the
+// current device for the NULL stream); nullptr on error. The first call for
+// a device looks the address up with that device current, then restores the
+// caller's current device.
+void* device_scratch(hipStream_t stream, int* status) {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    const hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         *status = PFS_ERR_LAUNCH;
         return nullptr;
     }
@@ -41,8 +46,18 @@ void* device_scratch(int* status) {
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     p = g_scratch[dev].load(std::memory_order_relaxed);
     if (!p) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) {
+            *status = PFS_ERR_LAUNCH;
+            return nullptr;
+        }
         void* addr = nullptr;
-        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+        const hipError_t found = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) {
+            *status = PFS_ERR_LAUNCH;
+            return nullptr;
+        }
+        if (found != hipSuccess || !addr) {
             *status = PFS_ERR_LAUNCH;
             return nullptr;
         }
@@ -67,7 +82,7 @@ int32_t pfs_verify_noalloc(const pfs_plan* plan, const void* q_fp16, const uint8
     if (!q_fp16 || !k_pool || !v_pool || !k_scale || !v_scale || !block_table || !live_len || !out_fp16)
         return PFS_ERR_NULL;  // before any HIP call
     int32_t st = PFS_OK;
-    void* ws = device_scratch(&st);
+    void* ws = device_scratch(reinterpret_cast<hipStream_t>(stream), &st);
     if (!ws) return st;
     return pfs_verify(plan, q_fp16, k_pool, v_pool, k_scale, v_scale, block_table, live_len, out_fp16, ws,
                       pfs::kNoallocScratchBytes, stream);
