@@ -281,6 +281,10 @@ int32_t pfs_kv_append(const pfs_plan* plan, const void* k_new_fp16, const void* 
         return PFS_ERR_ALIGNMENT;
     if (((uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)block_table | (uintptr_t)live_len) & 3u)
         return PFS_ERR_ALIGNMENT;
+    // one work-item per 8 values of a draft row: the grid's x extent (the
+    // plan's own split-grid bound already keeps this below 2^31)
+    if ((int64_t)plan->p.batch * plan->p.q * plan->p.num_kv_heads * (plan->p.head_dim / 8) > (int64_t)INT32_MAX)
+        return PFS_ERR_SHAPE;
     return pfs_launch_append(plan, k_new_fp16, v_new_fp16, k_scale, v_scale, block_table, live_len, k_pool, v_pool,
                              stream);
 }
