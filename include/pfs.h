@@ -315,7 +315,9 @@ int32_t pfs_dequant_paged(const pfs_plan* plan, const uint8_t* pool, const float
  * pools changes. Lengths are clamped into [0, capacity]; block-table entries
  * of the written tokens must lie in [0, num_pool_pages) (not checked on the
  * host). Uses the plan's batch, q, num_kv_heads, head_dim, page size,
- * strides and KV format. Enqueue only, no allocation; capturable.
+ * strides and KV format; batch * q * num_kv_heads * head_dim / 8 must stay
+ * below 2^31 (PFS_ERR_SHAPE otherwise; every plan pfs_plan_create accepts
+ * does). Enqueue only, no allocation; capturable.
  */
 int32_t pfs_kv_append(const pfs_plan* plan, const void* k_new_fp16, const void* v_new_fp16,
                       const float* k_scale, const float* v_scale, const int32_t* block_table,
