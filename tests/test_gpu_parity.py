@@ -317,3 +317,38 @@ def test_speculative_steps_in_one_graph():
         host.k_pool, host.v_pool = oracle.kv_append(host, knp, vnp)
         judge(yg, oracle_ref(host), f"graph step {s} lengths {host.live_len.tolist()}")
     del k_dev0, v_dev0
+
+
+@pytest.mark.parametrize("case", ["one-request", "batch"])
+def test_split_then_combine_is_verify(case):
+    """pfs_verify_split followed by pfs_verify_combine on the same stream,
+    plan and workspace gives the bytes of pfs_verify (include/pfs.h), and a
+    second combine over the same partials gives them again (the combine only
+    reads the workspace)."""
+    import torch
+
+    from paged_fp8_split_amd import _lib
+
+    if case == "one-request":
+        w = W.build(seed=61, batch=1, q=8, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                    lengths=[9000], outlier_frac=0.01)
+    else:
+        w = W.build(seed=62, batch=3, q=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=32,
+                    lengths=[3000, 0, 1700])
+    dev = device()
+    t = W.device_tensors(w, dev)
+    plan = pfs.make_plan(batch=w.batch, q=w.q, num_q_heads=w.num_q_heads, head_map=t["head_map"],
+                         k_pool=t["k_pool"], max_pages_per_row=w.max_pages_per_row, sm_scale=t["sm_scale"])
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    log(f"[two phases] {case}: {plan.num_splits} splits x {plan.tokens_per_split} tokens")
+    whole = to_np(run(w, tensors=t, workspace=ws)[0])
+    out = torch.full_like(t["q"], float("nan"))
+    _lib.verify_split(plan, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["block_table"], t["live_len"], ws)
+    _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws)
+    first = to_np(out).copy()
+    out.fill_(0.5)
+    _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws)
+    again = to_np(out)
+    judge(first, oracle_ref(w), f"two phases {case}")
+    assert np.array_equal(first.view(np.uint16), whole.view(np.uint16))
+    assert np.array_equal(again.view(np.uint16), whole.view(np.uint16))
