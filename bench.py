@@ -653,7 +653,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
-              "this build measures the single-GPU verify step only (no collectives, no sharding).", file=sys.stderr)
+              "bench.py measures the single-GPU verify step only (no collectives, no sharding).", file=sys.stderr)
         return 2
 
     import numpy as np

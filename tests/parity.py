@@ -1,4 +1,4 @@
-"""Shared helpers of the GPU tests: run the HIP path on a workload and judge
+"""Shared helpers of the GPU tests: run the HIP path on a workload and assert_parity
 its FP16 output against the FP64 oracle."""
 from __future__ import annotations
 
@@ -56,7 +56,7 @@ def fp16_ulp(r: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 10)
 
 
-def judge(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
+def assert_parity(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
     """Parity of GPU FP16 output y16 with the unrounded oracle result r."""
     y = y16.astype(np.float64)
     assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output"
@@ -82,7 +82,7 @@ def judge(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
     assert max_ulps_large <= 1.0, f"{what}: {max_ulps_large} ulp on |r| >= {LARGE}"
     return rep
 
-def judge_fp16_mode(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
+def assert_parity_fp16_mode(y16: np.ndarray, r: np.ndarray, what: str = "") -> dict:
     """The opt-in single-FP16-probability mode's own bar. Its FP16 rounding
     of each probability (2^-11 relative) can reach max abs ~4.1e-3 where
     attention concentrates on keys whose V values nearly cancel, so the mode

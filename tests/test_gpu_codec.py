@@ -11,7 +11,7 @@ import oracle
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, to_np
+from parity import device, assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,7 @@ def test_append_then_verify_matches_oracle():
     w2 = w.copy()
     w2.k_pool, w2.v_pool = oracle.kv_append(w, kn, vn)
     out, _ = run(w2, tensors=t)
-    judge(to_np(out), oracle_ref(w2), "append then verify")
+    assert_parity(to_np(out), oracle_ref(w2), "append then verify")
 
 
 @pytest.mark.parametrize("scale", [None, 1.0, 0.0011, 3.0e-7, 1.0 + 2.0 ** -12, 2.0 ** -9 * 3, 517.0])

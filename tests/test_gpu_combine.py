@@ -6,7 +6,7 @@ pfs_verify_combine). These cases give every head_dim a split count just above
 the row kernel's 32 (so that some blocks hold no split at all), counts that
 do not divide into the blocks, and a second request whose visible splits end
 inside a block, so that the combine selects out splits past the live length
-and merges blocks that hold nothing visible. Each output is judged against
+and merges blocks that hold nothing visible. Each output is checked against
 the FP64 oracle, and a second launch must give the same bytes. A request run
 alone and in a batch gives the same bytes too (both combine variants: first
 reads ahead of the live length for one request, after it in a batch)."""
@@ -16,7 +16,7 @@ import pytest
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, to_np
+from parity import device, assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def test_many_split_combine_matches_oracle(head_dim, splits):
     assert plan.num_splits == splits
     log(f"[combine] d{head_dim}: {splits} splits, lengths {lengths}")
     y1 = to_np(run(w, tokens_per_split=TPS, tensors=t)[0])
-    judge(y1, oracle_ref(w), f"many-split combine d{head_dim} s{splits}")
+    assert_parity(y1, oracle_ref(w), f"many-split combine d{head_dim} s{splits}")
     y2 = to_np(run(w, tokens_per_split=TPS, tensors=t)[0])
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
 
@@ -69,5 +69,5 @@ def test_a_request_does_not_depend_on_its_batch(head_dim, q, hq, hkv, tps, lengt
     alone = to_np(pfs.verify(t["q"][:1], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"][:1],
                              t["live_len"][:1], **kw))
     log(f"[batch invariance] d{head_dim} q{q} {hq}/{hkv} heads, {tps}-token splits, lengths {lengths}")
-    judge(both, oracle_ref(w), f"batch of two d{head_dim}")
+    assert_parity(both, oracle_ref(w), f"batch of two d{head_dim}")
     assert np.array_equal(alone[0].view(np.uint16), both[0].view(np.uint16))

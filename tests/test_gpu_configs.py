@@ -8,7 +8,7 @@ import pytest
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, sha, to_np
+from parity import device, assert_parity, log, oracle_ref, run, sha, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -17,9 +17,9 @@ def test_config1_literal_partitions_and_default_split():
     w = W.config(1)
     ref = oracle_ref(w)
     a = to_np(run(w, tokens_per_split=64)[0])   # one split per 64-token partition
-    judge(a, ref, "config1 tps=64")
+    assert_parity(a, ref, "config1 tps=64")
     b = to_np(run(w)[0])
-    judge(b, ref, "config1 default split")
+    assert_parity(b, ref, "config1 default split")
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
@@ -29,7 +29,7 @@ def test_long_context_configs(cfg):
     log(f"[config{cfg}] running GPU")
     y = to_np(run(w)[0])
     log(f"[config{cfg}] running oracle")
-    judge(y, oracle_ref(w), f"config{cfg}")
+    assert_parity(y, oracle_ref(w), f"config{cfg}")
 
 
 def test_config4_batch_with_retired_rows_and_relocation():
@@ -44,7 +44,7 @@ def test_config4_batch_with_retired_rows_and_relocation():
     y1 = to_np(run(w, tensors=t, workspace=ws)[0])
     retired = np.nonzero(w.live_len == 0)[0]
     assert len(retired) == 2 and np.all(y1[retired].view(np.uint16) == 0)
-    judge(y1, oracle_ref(w), "config4")
+    assert_parity(y1, oracle_ref(w), "config4")
     # relocate every page in place (same device buffers, same workspace)
     r = W.relocate(w, 777)
     t["k_pool"].untyped_storage().copy_(torch.from_numpy(r.k_pool).untyped_storage())
@@ -60,7 +60,7 @@ def test_config5_sweep_and_fp16_midpoints(q):
     log(f"[config5 q={q}] running")
     y = to_np(run(w)[0])
     ref = oracle_ref(w)
-    judge(y, ref, f"config5 q{q}")
+    assert_parity(y, ref, f"config5 q{q}")
     # the midpoint slot: request 0, KV head 0, last draft row (n = 2^16 keys):
     # the exact result is (1 + c * 2^-19) * 2^-6, an FP16 tie for c = 256, 768,
     # 1280, 1792; the GPU must round it like RNE(exact)
@@ -120,7 +120,7 @@ def test_determinism_eager_and_graph_replays(cfg, q):
     assert len(set(hashes)) == 1
     assert np.all(np.isfinite(eager.astype(np.float64)))
     if cfg in (1, 2):
-        judge(eager, oracle_ref(w), f"config{cfg} eager")
+        assert_parity(eager, oracle_ref(w), f"config{cfg} eager")
 
 
 def test_graph_replay_with_changed_lengths_and_pages():
@@ -156,7 +156,7 @@ def test_graph_replay_with_changed_lengths_and_pages():
         yg = to_np(out).copy()
         ye = to_np(run(wk, tensors=t)[0])
         assert np.array_equal(yg.view(np.uint16), ye.view(np.uint16)), f"case {k}"
-        judge(yg, oracle_ref(wk), f"replay lengths {lens}")
+        assert_parity(yg, oracle_ref(wk), f"replay lengths {lens}")
 
 
 @pytest.mark.parametrize("cus", [40, 80, 304])
@@ -184,4 +184,4 @@ def test_plans_for_other_compute_unit_counts(cus):
     pfs.verify(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"], t["live_len"],
                head_map=t["head_map"], sm_scale=t["sm_scale"], out=out, workspace=ws, plan=plan)
     log(f"[num_cus {cus}] {plan.num_splits} splits x {plan.tokens_per_split} tokens")
-    judge(to_np(out), oracle_ref(w), f"num_cus {cus}")
+    assert_parity(to_np(out), oracle_ref(w), f"num_cus {cus}")

@@ -11,7 +11,7 @@ import oracle
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, to_np
+from parity import device, assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_e5m2_parity(case):
     w = W.build(seed=zlib.crc32(name.encode()) % 1000 + 5, kv_format="e5m2", **kw)
     log(f"[e5m2] {name} tps={tps}")
     out, _ = run(w, tokens_per_split=tps)
-    judge(to_np(out), oracle_ref(w), "e5m2 " + name)
+    assert_parity(to_np(out), oracle_ref(w), "e5m2 " + name)
 
 
 def test_e5m2_256k_context():
@@ -54,7 +54,7 @@ def test_e5m2_256k_context():
     w = W.config(3, kv_format="e5m2")
     log("[e5m2] 256K context")
     y = to_np(run(w)[0])
-    judge(y, oracle_ref(w), "e5m2 256K")
+    assert_parity(y, oracle_ref(w), "e5m2 256K")
 
 
 def test_e5m2_infinity_and_nan_tails_do_not_leak():
@@ -63,7 +63,7 @@ def test_e5m2_infinity_and_nan_tails_do_not_leak():
     a = to_np(run(W.set_tail_sentinel(w, W.SENTINEL_NAN))[0])
     b = to_np(run(W.set_tail_sentinel(w, E5M2_INF))[0])
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
-    judge(a, oracle_ref(w), "e5m2 sentinels")
+    assert_parity(a, oracle_ref(w), "e5m2 sentinels")
 
 
 def test_e5m2_signed_scales():
@@ -71,7 +71,7 @@ def test_e5m2_signed_scales():
                 lengths=[700, 260], kv_format="e5m2")
     w.k_scale = (w.k_scale * np.array([-1.0, 0.0, 1.0, -1.0])).astype(np.float32)
     w.v_scale = (w.v_scale * np.array([1.0, -1.0, 1.0, -1.0])).astype(np.float32)
-    judge(to_np(run(w, tokens_per_split=128)[0]), oracle_ref(w), "e5m2 signed scales")
+    assert_parity(to_np(run(w, tokens_per_split=128)[0]), oracle_ref(w), "e5m2 signed scales")
 
 
 def test_e5m2_and_e4m3_of_the_same_bytes_differ():
@@ -83,8 +83,8 @@ def test_e5m2_and_e4m3_of_the_same_bytes_differ():
     w.v_pool &= 0xBF
     w5 = w.copy()
     w5.kv_format = "e5m2"
-    judge(to_np(run(w)[0]), oracle_ref(w), "bytes as e4m3")
-    judge(to_np(run(w5)[0]), oracle_ref(w5), "bytes as e5m2")
+    assert_parity(to_np(run(w)[0]), oracle_ref(w), "bytes as e4m3")
+    assert_parity(to_np(run(w5)[0]), oracle_ref(w5), "bytes as e5m2")
 
 
 @pytest.mark.parametrize("scale", [None, 1.0, 0.0011, 3.0e-7, 1.0 + 2.0 ** -12])
@@ -140,7 +140,7 @@ def test_e5m2_append_then_verify():
     w2 = w.copy()
     w2.k_pool, w2.v_pool = oracle.kv_append(w, kn, vn)
     out, _ = run(w2, tensors=t)
-    judge(to_np(out), oracle_ref(w2), "e5m2 append then verify")
+    assert_parity(to_np(out), oracle_ref(w2), "e5m2 append then verify")
 
 
 def test_float8_pool_dtypes_select_the_format():

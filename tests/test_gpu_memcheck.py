@@ -11,7 +11,7 @@ import pytest
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, to_np
+from parity import device, assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_canaries_around_every_buffer(context):
         assert _canaries_intact(b), f"canary of {k} overwritten"
     for k, h in before.items():
         assert np.array_equal(bufs[k].cpu().numpy(), h), f"read-only buffer {k} changed"
-    judge(to_np(out), oracle_ref(w), f"guarded context {context}")
+    assert_parity(to_np(out), oracle_ref(w), f"guarded context {context}")
 
 
 def test_256k_context_under_graph_replay_with_changed_lengths():
@@ -99,7 +99,7 @@ def test_256k_context_under_graph_replay_with_changed_lengths():
         if L == 0:
             assert np.all(yg.view(np.uint16) == 0)
         else:
-            judge(yg, oracle_ref(wk), f"256K graph replay L={L}")
+            assert_parity(yg, oracle_ref(wk), f"256K graph replay L={L}")
 
 
 # The outlier workload cut to a few thousand live tokens: attention
@@ -127,7 +127,7 @@ def _short_outlier_case(L, pv_mode):
 @pytest.mark.parametrize("L", SHORT_OUTLIER_LENGTHS)
 def test_default_mode_on_short_outlier_contexts(L):
     y, r = _short_outlier_case(L, "high_residual")
-    judge(y, r, f"default (high/residual), outlier workload at L={L}")
+    assert_parity(y, r, f"default (high/residual), outlier workload at L={L}")
 
 
 @pytest.mark.xfail(strict=True, reason="known limit of the opt-in fp16 mode: one FP16 probability operand "
@@ -135,5 +135,5 @@ def test_default_mode_on_short_outlier_contexts(L):
 @pytest.mark.parametrize("L", SHORT_OUTLIER_LENGTHS)
 def test_fp16_mode_on_short_outlier_contexts(L):
     y, r = _short_outlier_case(L, "fp16")
-    rep = judge(y, r, f"fp16 mode, outlier workload at L={L}")
+    rep = assert_parity(y, r, f"fp16 mode, outlier workload at L={L}")
     log(f"[known] {rep}")

@@ -9,7 +9,7 @@ import oracle
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, run, to_np
+from parity import device, assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,7 @@ def test_small_parity(case):
     w = W.build(seed=zlib.crc32(name.encode()) % 1000, **kw)
     log(f"[small] {name} tps={tps}")
     out, _ = run(w, tokens_per_split=tps)
-    judge(to_np(out), oracle_ref(w), name)
+    assert_parity(to_np(out), oracle_ref(w), name)
 
 
 def test_rows_without_visible_keys_are_positive_zero():
@@ -98,7 +98,7 @@ def test_rows_without_visible_keys_are_positive_zero():
     assert np.all(bits[0] == 0)           # retired request
     assert np.all(bits[1, :3] == 0)       # rows that see nothing (L < q)
     assert np.all(out[1, 3:] != 0)
-    judge(out, oracle_ref(w), "zero rows")
+    assert_parity(out, oracle_ref(w), "zero rows")
 
 
 def test_head_major_pool_matches_token_major_bitwise():
@@ -108,7 +108,7 @@ def test_head_major_pool_matches_token_major_bitwise():
                 lengths=[3000, 700])
     y, t = run(w)
     ya = to_np(y)
-    judge(ya, oracle_ref(w), "token-major")
+    assert_parity(ya, oracle_ref(w), "token-major")
     kh = t["k_pool"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     vh = t["v_pool"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     log(f"[layout] head-major strides {tuple(kh.stride())}")
@@ -129,7 +129,7 @@ def test_negative_and_zero_scales():
     log(f"[scales] k={w.k_scale.tolist()} v={w.v_scale.tolist()}")
     for tps in (0, 128):
         out = to_np(run(w, tokens_per_split=tps)[0])
-        judge(out, oracle_ref(w), f"signed scales tps={tps}")
+        assert_parity(out, oracle_ref(w), f"signed scales tps={tps}")
 
 
 def test_padded_strides_match_contiguous_bitwise():
@@ -138,7 +138,7 @@ def test_padded_strides_match_contiguous_bitwise():
     variants = [W.build(seed=41, token_pad=16, **kw), W.build(seed=41, page_pad=16 * 7, **kw),
                 W.build(seed=41, token_pad=512, page_pad=256, **kw)]
     ya = to_np(run(a)[0])
-    judge(ya, oracle_ref(a), "contiguous")
+    assert_parity(ya, oracle_ref(a), "contiguous")
     for v in variants:
         yv = to_np(run(v)[0])
         assert np.array_equal(ya.view(np.uint16), yv.view(np.uint16)), (v.token_stride, v.page_stride)
@@ -150,7 +150,7 @@ def test_tail_sentinels_do_not_leak():
     a = to_np(run(W.set_tail_sentinel(w, W.SENTINEL_NAN))[0])
     b = to_np(run(W.set_tail_sentinel(w, W.SENTINEL_MAX))[0])
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
-    judge(a, oracle_ref(w), "sentinels")
+    assert_parity(a, oracle_ref(w), "sentinels")
 
 
 def test_power_of_two_v_scale_is_exact():
@@ -196,7 +196,7 @@ def test_output_guard_bytes_untouched():
     run(w, tensors=t, out=out)
     host = to_np(buf)
     assert np.all(host[:guard] == np.float16(12345.0)) and np.all(host[guard + n:] == np.float16(12345.0))
-    judge(host[guard:guard + n].reshape(out.shape), oracle_ref(w), "guarded out")
+    assert_parity(host[guard:guard + n].reshape(out.shape), oracle_ref(w), "guarded out")
 
 
 def test_two_streams_two_workspaces():
@@ -230,7 +230,7 @@ def test_page_sizes_of_the_pages(page):
                 lengths=[3 * page + 37, page - 3])
     log(f"[page] {page} lengths={w.live_len.tolist()}")
     for tps in (0, 640):
-        judge(to_np(run(w, tokens_per_split=tps)[0]), oracle_ref(w), f"page {page} tps={tps}")
+        assert_parity(to_np(run(w, tokens_per_split=tps)[0]), oracle_ref(w), f"page {page} tps={tps}")
 
 
 def test_largest_split_uses_the_whole_tile_table():
@@ -239,7 +239,7 @@ def test_largest_split_uses_the_whole_tile_table():
     w = W.build(seed=71, batch=1, q=8, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=64,
                 lengths=[2 * 16384 + 1000])
     log("[tps] 16384")
-    judge(to_np(run(w, tokens_per_split=16384)[0]), oracle_ref(w), "tps 16384")
+    assert_parity(to_np(run(w, tokens_per_split=16384)[0]), oracle_ref(w), "tps 16384")
 
 
 def test_most_rows_per_kv_head():
@@ -247,10 +247,10 @@ def test_most_rows_per_kv_head():
     blocks of 64 at head_dim 256, and the most query heads (256) at head_dim 64."""
     w = W.build(seed=72, batch=1, q=16, num_q_heads=16, num_kv_heads=1, head_dim=256, page_size=64,
                 lengths=[1500])
-    judge(to_np(run(w)[0]), oracle_ref(w), "256 rows d256")
+    assert_parity(to_np(run(w)[0]), oracle_ref(w), "256 rows d256")
     w2 = W.build(seed=73, batch=1, q=2, num_q_heads=256, num_kv_heads=2, head_dim=64, page_size=16,
                  lengths=[700])
-    judge(to_np(run(w2)[0]), oracle_ref(w2), "256 query heads d64")
+    assert_parity(to_np(run(w2)[0]), oracle_ref(w2), "256 query heads d64")
 
 
 def test_lengths_at_split_partition_and_tile_edges():
@@ -261,7 +261,7 @@ def test_lengths_at_split_partition_and_tile_edges():
                 lengths=lengths)
     r = oracle_ref(w)
     for tps in (0, 256, 64):
-        judge(to_np(run(w, tokens_per_split=tps)[0]), r, f"edge lengths tps={tps}")
+        assert_parity(to_np(run(w, tokens_per_split=tps)[0]), r, f"edge lengths tps={tps}")
 
 
 def test_speculative_steps_in_one_graph():
@@ -315,7 +315,7 @@ def test_speculative_steps_in_one_graph():
         assert np.array_equal(to_np(out).view(np.uint16), yg.view(np.uint16)), f"step {s}"
         assert torch.equal(kg, t["k_pool"]) and torch.equal(vg, t["v_pool"]), f"step {s} pools"
         host.k_pool, host.v_pool = oracle.kv_append(host, knp, vnp)
-        judge(yg, oracle_ref(host), f"graph step {s} lengths {host.live_len.tolist()}")
+        assert_parity(yg, oracle_ref(host), f"graph step {s} lengths {host.live_len.tolist()}")
     del k_dev0, v_dev0
 
 
@@ -349,6 +349,6 @@ def test_split_then_combine_is_verify(case):
     out.fill_(0.5)
     _lib.verify_combine(plan, t["v_scale"], t["live_len"], out, ws)
     again = to_np(out)
-    judge(first, oracle_ref(w), f"two phases {case}")
+    assert_parity(first, oracle_ref(w), f"two phases {case}")
     assert np.array_equal(first.view(np.uint16), whole.view(np.uint16))
     assert np.array_equal(again.view(np.uint16), whole.view(np.uint16))

@@ -6,8 +6,8 @@ same V operand (the other GPU tests all run it); the opt-in fp16 mode carries
 the high part alone. Both meet the bar against the FP64 oracle on these
 shapes and are bit-identical across launches; the default's FP16 outputs
 disagree with the correctly rounded oracle result less often. The default is
-held to the full bar (parity.judge); the opt-in mode to its own documented
-one (parity.judge_fp16_mode), since its single FP16 operand can miss max abs
+held to the full bar (parity.assert_parity); the opt-in mode to its own documented
+one (parity.assert_parity_fp16_mode), since its single FP16 operand can miss max abs
 4e-3 where attention concentrates on nearly cancelling V values."""
 import zlib
 
@@ -17,7 +17,7 @@ import pytest
 import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, judge_fp16_mode, log, oracle_ref, to_np
+from parity import device, assert_parity, assert_parity_fp16_mode, log, oracle_ref, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_mode_parity(case, residual):
     w = W.build(seed=zlib.crc32(name.encode()) % 1000 + 11, **kw)
     log(f"[pv mode] {name} tps={tps} residual={residual}")
     y, _ = run_mode(w, residual, tps)
-    (judge if residual else judge_fp16_mode)(y, oracle_ref(w), ("residual " if residual else "fp16 ") + name)
+    (assert_parity if residual else assert_parity_fp16_mode)(y, oracle_ref(w), ("residual " if residual else "fp16 ") + name)
 
 
 def test_modes_are_deterministic_and_differ():
@@ -81,7 +81,7 @@ def test_e5m2_in_both_modes(residual):
     w = W.build(seed=92, batch=2, q=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
                 lengths=[1500, 77], kv_format="e5m2", outlier_frac=0.02)
     y, _ = run_mode(w, residual, 256)
-    (judge if residual else judge_fp16_mode)(y, oracle_ref(w), ("residual" if residual else "fp16") + " e5m2")
+    (assert_parity if residual else assert_parity_fp16_mode)(y, oracle_ref(w), ("residual" if residual else "fp16") + " e5m2")
 
 
 @pytest.mark.parametrize("cfg,q", [(2, None), (3, None), (5, 8)])
@@ -94,8 +94,8 @@ def test_full_size_disagreements(cfg, q):
     r = oracle_ref(w)
     y1, t = run_mode(w, False)
     y2, _ = run_mode(w, True, tensors=t)
-    judge(y2, r, f"residual {w.name}")
-    judge_fp16_mode(y1, r, f"fp16 {w.name}")
+    assert_parity(y2, r, f"residual {w.name}")
+    assert_parity_fp16_mode(y1, r, f"fp16 {w.name}")
     d1, d2 = disagreements(y1, r), disagreements(y2, r)
     log(f"[pv mode] {w.name}: FP16 disagreements with RNE(oracle): fp16 {d1}, high_residual {d2} of {r.size}")
     assert d2 <= d1

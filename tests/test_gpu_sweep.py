@@ -11,7 +11,7 @@ import pytest
 
 from paged_fp8_split_amd import workloads as W
 
-from parity import judge, log, oracle_ref, run, to_np
+from parity import assert_parity, log, oracle_ref, run, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_random_shape_parity(k):
     b = to_np(run(w, tokens_per_split=tps, tensors=t)[0])
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), "repeat launch differs"
     r = oracle_ref(w)
-    judge(a, r, f"sweep {k}")
+    assert_parity(a, r, f"sweep {k}")
     # rows that see no key are +0.0
     L = np.clip(w.live_len.astype(np.int64), 0, w.capacity)
     for bb in range(w.batch):
@@ -86,4 +86,4 @@ def test_medium_batch_parity_default_plan(k):
     a = to_np(out)
     b = to_np(run(w, tensors=t)[0])
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), "repeat launch differs"
-    judge(a, oracle_ref(w), f"medium {k}")
+    assert_parity(a, oracle_ref(w), f"medium {k}")

@@ -10,7 +10,7 @@ import paged_fp8_split_amd as pfs
 from paged_fp8_split_amd import _lib
 from paged_fp8_split_amd import workloads as W
 
-from parity import device, judge, log, oracle_ref, to_np
+from parity import device, assert_parity, log, oracle_ref, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def test_noalloc_matches_verify_on_two_calls_the_second_smaller():
         log(f"[noalloc] {name}: {w.name}")
         y, yref = _both(w)
         assert np.array_equal(y.view(np.uint16), yref.view(np.uint16)), name
-        judge(y, oracle_ref(w), f"noalloc {name}")
+        assert_parity(y, oracle_ref(w), f"noalloc {name}")
 
 
 def test_noalloc_refuses_a_plan_beyond_its_array():
