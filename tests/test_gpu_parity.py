@@ -352,3 +352,42 @@ def test_split_then_combine_is_verify(case):
     assert_parity(first, oracle_ref(w), f"two phases {case}")
     assert np.array_equal(first.view(np.uint16), whole.view(np.uint16))
     assert np.array_equal(again.view(np.uint16), whole.view(np.uint16))
+
+
+@pytest.mark.parametrize("case", ["interleaved", "shuffled"])
+def test_non_contiguous_head_maps(case):
+    """A KV head's query heads need not be adjacent (any map with uniform
+    groups, include/pfs.h). With the map m(h) = c(pi(h)) -- c the contiguous
+    map h // G, pi a permutation of the query heads -- and the query heads
+    permuted the same way, query head h gives the bytes that head pi(h) gives
+    under c: each row's arithmetic does not depend on where the map puts it."""
+    import dataclasses
+
+    base = W.build(seed=83, batch=2, q=4, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=32,
+                   lengths=[900, 333], outlier_frac=0.01)
+    hq, G = base.num_q_heads, base.group
+    if case == "interleaved":  # query heads g, g + 4, g + 8, g + 12 share KV head g
+        pi = np.array([(h % 4) * G + h // 4 for h in range(hq)])
+    else:
+        pi = np.random.default_rng(5).permutation(hq)
+    c = np.arange(hq) // G
+    w = dataclasses.replace(base, head_map=c[pi].astype(np.int32), q_fp16=np.ascontiguousarray(base.q_fp16[:, :, pi]))
+    log(f"[head map] {case}: {w.head_map.tolist()}")
+    y_base = to_np(run(base)[0])
+    y = to_np(run(w)[0])
+    assert_parity(y, oracle_ref(w), f"{case} head map")
+    assert np.array_equal(y.view(np.uint16), y_base[:, :, pi].view(np.uint16))
+
+
+def test_widest_group_and_widest_multi_head():
+    """The extremes of the head map: all 256 query heads on one KV head at
+    q = 16 (4,096 rows per KV head, 16 row blocks), and 256 KV heads with one
+    query head each (one row per KV head, padded to a 16-row tile)."""
+    w = W.build(seed=84, batch=1, q=16, num_q_heads=256, num_kv_heads=1, head_dim=64, page_size=16,
+                lengths=[300])
+    log("[heads] 256 query heads on one KV head, q16")
+    assert_parity(to_np(run(w)[0]), oracle_ref(w), "group of 256")
+    w2 = W.build(seed=85, batch=2, q=1, num_q_heads=256, num_kv_heads=256, head_dim=128, page_size=32,
+                 lengths=[520, 77])
+    log("[heads] 256 KV heads, q1")
+    assert_parity(to_np(run(w2)[0]), oracle_ref(w2), "256 KV heads")
