@@ -391,3 +391,19 @@ def test_widest_group_and_widest_multi_head():
                  lengths=[520, 77])
     log("[heads] 256 KV heads, q1")
     assert_parity(to_np(run(w2)[0]), oracle_ref(w2), "256 KV heads")
+
+
+@pytest.mark.parametrize("sm_scale", [1.0e-3, 1.0, 3.0])
+def test_softmax_scales(sm_scale):
+    """Softmax scales far from 1/sqrt(head_dim): a tiny one (near-uniform
+    attention over every visible key) and large ones (scores spread over
+    hundreds of log2 units, so the lazily raised reference maximum moves
+    often and most probabilities underflow), each against the oracle."""
+    import dataclasses
+
+    w = W.build(seed=86, batch=2, q=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=32,
+                lengths=[2500, 700], outlier_frac=0.01)
+    w = dataclasses.replace(w, sm_scale=sm_scale)
+    log(f"[sm_scale] {sm_scale}")
+    for tps in (0, 256):
+        assert_parity(to_np(run(w, tokens_per_split=tps)[0]), oracle_ref(w), f"sm_scale {sm_scale} tps={tps}")
