@@ -399,3 +399,20 @@ def test_package_codec_calls_check_every_tensor_before_the_library():
         assert "GPU" not in str(e.value), over
     with pytest.raises(ValueError, match="GPU"):
         pfs.kv_append(kn, kn, ks, vs, bt, ll, kp, vp)
+
+
+def test_header_compiles_as_c99_and_a_c_client_runs(tmp_path):
+    """include/pfs.h is plain C: a C99 client (tests/abi_c_client.c) compiles
+    against it with every warning an error, links libpfs.so and plans a
+    shape through the ABI with no Python in between."""
+    import subprocess
+
+    lib = _lib.LIB_PATH
+    exe = str(tmp_path / "abi_c_client")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "abi_c_client.c"), "-o", exe, lib,
+                    "-Wl,-rpath," + os.path.dirname(lib)], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "splits 128 tokens_per_split 2048 workspace 16908288" in res.stdout
+    assert "token stride 264: a KV stride or a base pointer is not 16-byte aligned" in res.stdout
