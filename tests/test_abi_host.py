@@ -416,3 +416,38 @@ def test_header_compiles_as_c99_and_a_c_client_runs(tmp_path):
     assert res.returncode == 0, res.stdout + res.stderr
     assert "splits 128 tokens_per_split 2048 workspace 16908288" in res.stdout
     assert "token stride 264: a KV stride or a base pointer is not 16-byte aligned" in res.stdout
+
+
+def test_oracle_and_product_share_no_code():
+    """The oracle (oracle/) and the product (paged_fp8_split_amd/, include/)
+    are independent: no product source imports, includes or loads anything
+    from oracle/, the oracle imports nothing from the product, and their C
+    and HIP sources include only system headers and their own files. The
+    input generator (paged_fp8_split_amd/workloads.py) is the one module both
+    sides may use; the oracle takes its workloads as plain objects."""
+    import ast
+    import glob
+
+    def py_imports(path):
+        mods = set()
+        for node in ast.walk(ast.parse(open(path).read())):
+            if isinstance(node, ast.Import):
+                mods.update(a.name.split(".")[0] for a in node.names)
+            elif isinstance(node, ast.ImportFrom) and node.module and node.level == 0:
+                mods.add(node.module.split(".")[0])
+        return mods
+
+    product_py = glob.glob(os.path.join(ROOT, "paged_fp8_split_amd", "*.py"))
+    for f in product_py:
+        assert "oracle" not in py_imports(f), f
+        assert "liboracle" not in open(f).read(), f
+    for f in glob.glob(os.path.join(ROOT, "oracle", "*.py")):
+        assert "paged_fp8_split_amd" not in py_imports(f), f
+    includes = re.compile(r'^\s*#\s*include\s*"([^"]+)"', re.M)
+    for f in glob.glob(os.path.join(ROOT, "oracle", "*.c")) + glob.glob(os.path.join(ROOT, "oracle", "*.h")):
+        assert includes.findall(open(f).read()) == [], f  # system headers only
+    for f in glob.glob(os.path.join(ROOT, "paged_fp8_split_amd", "csrc", "*")):
+        for inc in includes.findall(open(f).read()):
+            assert "oracle" not in inc, (f, inc)
+    for f in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        assert "oracle" not in open(f).read().lower(), f
