@@ -451,3 +451,17 @@ def test_oracle_and_product_share_no_code():
             assert "oracle" not in inc, (f, inc)
     for f in glob.glob(os.path.join(ROOT, "include", "*.h")):
         assert "oracle" not in open(f).read().lower(), f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libpfs.so nothing runs: loading raises, and so does the package's
+    verify (no fallback computes anything)."""
+    import paged_fp8_split_amd as pfs
+
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libpfs.so"))
+    monkeypatch.setattr(pfs, "_plans", {})
+    with pytest.raises(RuntimeError, match="is not built"):
+        _lib.load()
+    with pytest.raises(RuntimeError, match="is not built"):
+        pfs.verify(**_host_problem())
