@@ -407,3 +407,15 @@ def test_softmax_scales(sm_scale):
     log(f"[sm_scale] {sm_scale}")
     for tps in (0, 256):
         assert_parity(to_np(run(w, tokens_per_split=tps)[0]), oracle_ref(w), f"sm_scale {sm_scale} tps={tps}")
+
+
+def test_million_token_context():
+    """One request of 2^20 live tokens (four times the metric's context), with
+    1 % outlier tokens: the default plan (256 splits) and the largest split
+    (64 splits of 16,384 tokens), each against the oracle."""
+    w = W.build(seed=87, batch=1, q=2, num_q_heads=4, num_kv_heads=1, head_dim=64, page_size=64,
+                lengths=[1 << 20], outlier_frac=0.01)
+    ref = oracle_ref(w)
+    for tps in (0, 16384):
+        log(f"[1M context] tps={tps}")
+        assert_parity(to_np(run(w, tokens_per_split=tps)[0]), ref, f"1M context tps={tps}")
