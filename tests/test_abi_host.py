@@ -465,3 +465,78 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         _lib.load()
     with pytest.raises(RuntimeError, match="is not built"):
         pfs.verify(**_host_problem())
+
+
+def _plan_or_status(batch, q, hkv, G, D, page, ppr, pool, tps, fmt, mode, cus, pad, sm):
+    hq = hkv * G
+    token_stride = hkv * D + pad
+    kw = dict(batch=batch, q=q, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=page,
+              max_pages_per_row=ppr, num_pool_pages=pool, kv_page_stride=page * token_stride,
+              kv_token_stride=token_stride, kv_head_stride=D, sm_scale=sm,
+              head_map=[h // G for h in range(hq)] if G > 0 else [], tokens_per_split=tps, kv_format=fmt,
+              pv_mode=mode, num_cus=cus)
+    try:
+        return _lib.Plan(**kw), 0
+    except _lib.PfsError as e:
+        return None, e.status
+
+
+def test_plan_create_on_random_problems():
+    """pfs_plan_create on random problems, most of them invalid in some field:
+    it always returns one of its status codes (no crash, no other value)."""
+    from hypothesis import HealthCheck, given, settings
+    from hypothesis import strategies as st
+
+    codes = set(_lib.STATUS)
+
+    @settings(max_examples=300, deadline=None, database=None, suppress_health_check=list(HealthCheck))
+    @given(batch=st.integers(-2, 70000), q=st.integers(-1, 18), hkv=st.sampled_from([1, 2, 3, 4, 8, 16, 256, 257]),
+           G=st.integers(0, 17), D=st.sampled_from([0, 32, 64, 96, 128, 256, 512]),
+           page=st.sampled_from([0, 8, 16, 48, 64, 848, 3456]), ppr=st.integers(-1, 1 << 20),
+           pool=st.integers(-1, 1 << 16), tps=st.sampled_from([0, 64, 100, 256, 2048, 16384, 16448]),
+           fmt=st.integers(-1, 2), mode=st.integers(-1, 2), cus=st.integers(-1, 400),
+           pad=st.sampled_from([0, 8, 16, 256]), sm=st.sampled_from([0.0, -1.0, 0.0625, float("inf"), float("nan")]))
+    def check(**kw):
+        plan, status = _plan_or_status(**kw)
+        assert status in codes and (plan is not None) == (status == 0)
+
+    check()
+
+
+def test_plans_of_valid_problems_keep_their_invariants():
+    """Problems drawn from the supported ranges: each is planned (or refused
+    only because its split grid would pass 2^31 work-items), and every plan
+    covers the capacity with whole 64-token partitions, keeps a split within
+    the 1024-tile table, uses no empty trailing split, and sizes the
+    workspace as (max, sum) pairs plus D accumulators per (split, request, KV
+    head, row), each array 256-byte aligned."""
+    from hypothesis import HealthCheck, given, settings
+    from hypothesis import strategies as st
+
+    accepted = []
+
+    @settings(max_examples=300, deadline=None, database=None, suppress_health_check=list(HealthCheck))
+    @given(batch=st.integers(0, 65535), q=st.integers(1, 16), hkv=st.sampled_from([1, 2, 4, 8]),
+           G=st.integers(1, 16), D=st.sampled_from([64, 128, 256]), page=st.sampled_from([16, 64, 848, 3456]),
+           ppr=st.integers(1, 4096), pool=st.integers(1, 65536), tps=st.sampled_from([0, 0, 0, 64, 256, 2048, 16384]),
+           fmt=st.integers(0, 1), mode=st.integers(0, 1), cus=st.sampled_from([0, 40, 256, 304]),
+           pad=st.sampled_from([0, 16, 256]), sm=st.just(0.0625))
+    def check(batch, q, hkv, G, D, page, ppr, pool, tps, fmt, mode, cus, pad, sm):
+        plan, status = _plan_or_status(batch, q, hkv, G, D, page, ppr, pool, tps, fmt, mode, cus, pad, sm)
+        if plan is None:
+            assert status == _lib.STATUS_CODE["PFS_ERR_SHAPE"]
+            return
+        accepted.append(1)
+        cap = ppr * page
+        assert p_ok(plan, cap)
+        slots = plan.num_splits * max(batch, 1) * hkv * G * q
+        rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        assert plan.workspace_bytes == rnd(slots * 2 * 4) + rnd(slots * D * 4)
+
+    def p_ok(plan, cap):
+        t = plan.tokens_per_split
+        return (t % 64 == 0 and 64 <= t <= 16384 and plan.num_splits >= 1 and plan.num_splits * t >= cap
+                and (plan.num_splits - 1) * t < cap)
+
+    check()
+    assert len(accepted) >= 150, len(accepted)
