@@ -540,3 +540,21 @@ def test_plans_of_valid_problems_keep_their_invariants():
 
     check()
     assert len(accepted) >= 150, len(accepted)
+
+
+def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The host planner built with -fsanitize=address,undefined (g++, host
+    code only) and driven by tests/plan_fuzz.cpp: random problems, the
+    invariants of every accepted plan and the host-side error paths of the
+    other calls, with no sanitizer report and no kernel launch reached."""
+    import subprocess
+
+    exe = str(tmp_path / "plan_fuzz")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "paged_fp8_split_amd", "csrc", "pfs_plan.cpp"),
+                    os.path.join(ROOT, "tests", "plan_fuzz.cpp"), "-o", exe], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
+    res = subprocess.run([exe, "30000"], capture_output=True, text=True, timeout=300, env=env)
+    assert res.returncode == 0, res.stdout + res.stderr
+    m = re.search(r"plans (\d+) of 30000, launches 0", res.stdout)
+    assert m and int(m.group(1)) > 1000, res.stdout
