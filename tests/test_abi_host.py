@@ -555,6 +555,8 @@ def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
                     os.path.join(ROOT, "tests", "plan_fuzz.cpp"), "-o", exe], check=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
     res = subprocess.run([exe, "30000"], capture_output=True, text=True, timeout=300, env=env)
+    if "does not come first in initial library list" in res.stderr:
+        pytest.skip("the environment preloads a library ahead of the AddressSanitizer runtime")
     assert res.returncode == 0, res.stdout + res.stderr
     m = re.search(r"plans (\d+) of 30000, launches 0", res.stdout)
     assert m and int(m.group(1)) > 1000, res.stdout
